@@ -1,0 +1,155 @@
+// Block-Sparse index estimation.
+//
+// PaperTrace 2.1.2 "MInference", section 2 (Eq. 6 and the mean-pooling proxy)
+// and blog-zz7 "LLM模型之MInference" section 2.3.2: Q and K are mean-pooled
+// over 64-token blocks, the block scores r_uv = scale * Qbar_u . Kbar_v are
+// formed for v <= u, and every query block keeps its top-k_b key blocks.
+// Forced blocks (first / diagonal) take an infinite score, so they occupy
+// budget slots.  Everything is fp32 and free of floating-point atomics.
+//
+// GPU plan: a pooling pass streams Q (BS heads) and K (their KV heads) once
+// from HBM; a tiled fp32 product writes the causal score tiles of a batch of
+// heads into the workspace (so the score matrix never has to be resident for
+// the whole layer); one work-group per (head, query block) then runs the
+// exact radix top-k on its row.
+#include "kernels.h"
+#include "topk.h"
+
+namespace minf {
+
+namespace {
+
+struct BsBatch {
+  int32_t count;
+  int32_t bh[64];      // b * Hq + h of each head in this batch
+};
+
+// grid (nq, B*Hq + B*Hkv): mean of each 64-row block of Q (BS heads) and K.
+template <typename T, int DH>
+__global__ __launch_bounds__(DH) void bs_pool_kernel(BsParams P, uint64_t kv_used) {
+  const int u = blockIdx.x;
+  const int y = blockIdx.y;
+  const int BHq = P.B * P.Hq;
+  const T* src;
+  float* dst;
+  if (y < BHq) {
+    const int h = y % P.Hq;
+    if (P.ht.kind[h] != MINF_BSPARSE) return;
+    src = reinterpret_cast<const T*>(P.Q) + (size_t)y * P.n * DH;
+    dst = P.qbar + ((size_t)y * P.nq + u) * DH;
+  } else {
+    const int z = y - BHq;
+    const int kv = z % P.Hkv;
+    if (!((kv_used >> kv) & 1ull)) return;
+    src = reinterpret_cast<const T*>(P.K) + (size_t)z * P.n * DH;
+    dst = P.kbar + ((size_t)z * P.nq + u) * DH;
+  }
+  const int r0 = 64 * u, r1 = min(r0 + 64, P.n);
+  const int d = threadIdx.x;
+  float acc = 0.f;
+  for (int r = r0; r < r1; ++r) {
+    if constexpr (sizeof(T) == 2) acc += bf16_to_f32(src[(size_t)r * DH + d]);
+    else acc += src[(size_t)r * DH + d];
+  }
+  dst[d] = acc / (float)(r1 - r0);
+}
+
+// grid (tiles_v, tiles_u, batch): 64x64 causal tiles of R = scale * Qbar Kbar^T.
+template <int DH>
+__global__ __launch_bounds__(256) void bs_score_kernel(BsParams P, BsBatch batch) {
+  const int tv = blockIdx.x, tu = blockIdx.y;
+  if (tv > tu) return;
+  const int bh = batch.bh[blockIdx.z];
+  const int b = bh / P.Hq, h = bh % P.Hq;
+  const int kv = h / (P.Hq / P.Hkv);
+  const float* A = P.qbar + (size_t)bh * P.nq * DH;
+  const float* Bm = P.kbar + ((size_t)b * P.Hkv + kv) * P.nq * DH;
+  float* R = P.scores + (size_t)blockIdx.z * P.nq * P.nq;
+  __shared__ float sa[16][65], sb[16][65];
+  const int tx = threadIdx.x & 15, ty = threadIdx.x >> 4;
+  float acc[4][4] = {};
+  for (int k0 = 0; k0 < DH; k0 += 16) {
+    for (int i = threadIdx.x; i < 64 * 16; i += 256) {
+      const int r = i >> 4, kk = i & 15;
+      const int ua = 64 * tu + r, vb = 64 * tv + r;
+      sa[kk][r] = ua < P.nq ? A[(size_t)ua * DH + k0 + kk] : 0.f;
+      sb[kk][r] = vb < P.nq ? Bm[(size_t)vb * DH + k0 + kk] : 0.f;
+    }
+    __syncthreads();
+    #pragma unroll
+    for (int kk = 0; kk < 16; ++kk) {
+      float a[4], bv[4];
+      #pragma unroll
+      for (int i = 0; i < 4; ++i) { a[i] = sa[kk][ty + 16 * i]; bv[i] = sb[kk][tx + 16 * i]; }
+      #pragma unroll
+      for (int i = 0; i < 4; ++i)
+        #pragma unroll
+        for (int jx = 0; jx < 4; ++jx) acc[i][jx] = __builtin_fmaf(a[i], bv[jx], acc[i][jx]);
+    }
+    __syncthreads();
+  }
+  #pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int uu = 64 * tu + ty + 16 * i;
+    if (uu >= P.nq) continue;
+    #pragma unroll
+    for (int jx = 0; jx < 4; ++jx) {
+      const int vv = 64 * tv + tx + 16 * jx;
+      if (vv <= uu) R[(size_t)uu * P.nq + vv] = P.scale * acc[i][jx];
+    }
+  }
+}
+
+// grid (nq, batch): exact top-k of row u over v <= u.
+__global__ __launch_bounds__(256) void bs_topk_kernel(BsParams P, BsBatch batch) {
+  const int u = blockIdx.x;
+  const int bh = batch.bh[blockIdx.y];
+  const int h = bh % P.Hq;
+  __shared__ TopkShared sh;
+  const float* row = P.scores + ((size_t)blockIdx.y * P.nq + u) * P.nq;
+  const int force = P.ht.b[h];
+  const float inf = __builtin_huge_valf();
+  const int k = min(P.ht.a[h], u + 1);
+  int32_t* out = P.blk_idx + ((size_t)bh * P.nq + u) * P.max_kb;
+  block_topk<256, 8>(
+      [&](int v) {
+        if (((force & MINF_FORCE_FIRST_BLOCK) && v == 0) || ((force & MINF_FORCE_DIAG_BLOCK) && v == u)) return inf;
+        return row[v];
+      },
+      u + 1, k, out, (int)P.max_kb, sh);
+  if (threadIdx.x == 0) P.blk_cnt[(size_t)bh * P.nq + u] = k;
+}
+
+template <typename T, int DH>
+hipError_t launch_t(const BsParams& p, hipStream_t st) {
+  uint64_t kv_used = 0;
+  for (int h = 0; h < p.Hq; ++h)
+    if (p.ht.kind[h] == MINF_BSPARSE) kv_used |= 1ull << (h / (p.Hq / p.Hkv));
+  hipLaunchKernelGGL((bs_pool_kernel<T, DH>), dim3(p.nq, p.B * (p.Hq + p.Hkv)), dim3(DH), 0, st, p, kv_used);
+  BsBatch batch{};
+  const int tiles = (p.nq + 63) / 64;
+  auto flush = [&]() {
+    if (!batch.count) return;
+    hipLaunchKernelGGL((bs_score_kernel<DH>), dim3(tiles, tiles, batch.count), dim3(256), 0, st, p, batch);
+    hipLaunchKernelGGL(bs_topk_kernel, dim3(p.nq, batch.count), dim3(256), 0, st, p, batch);
+    batch.count = 0;
+  };
+  const int cap = (int)std::min<int64_t>(p.score_heads, 64);
+  for (int b = 0; b < p.B; ++b)
+    for (int h = 0; h < p.Hq; ++h) {
+      if (p.ht.kind[h] != MINF_BSPARSE) continue;
+      batch.bh[batch.count++] = b * p.Hq + h;
+      if (batch.count == cap) flush();
+    }
+  flush();
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_bs_index(const BsParams& p, hipStream_t st) {
+  if (p.in_bf16) return p.dh == 128 ? launch_t<uint16_t, 128>(p, st) : launch_t<uint16_t, 64>(p, st);
+  return p.dh == 128 ? launch_t<float, 128>(p, st) : launch_t<float, 64>(p, st);
+}
+
+}  // namespace minf

@@ -1,0 +1,299 @@
+// Host side of the C interface declared in include/minf.h: argument checks,
+// size queries, workspace layout and kernel launches.  No device memory is
+// allocated and the host never waits on the GPU.
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <algorithm>
+
+#include "common.h"
+#include "kernels.h"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+minf_status fail(minf_status s, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof g_err, fmt, ap);
+  va_end(ap);
+  return s;
+}
+
+int64_t round_up(int64_t x, int64_t m) { return (x + m - 1) / m * m; }
+
+struct Derived {
+  int64_t nq = 0, max_v = 0, max_s = 0, max_kb = 0, max_chunks = 0, bm_words = 0;
+  bool has_a = false, has_vs = false, has_bs = false;
+  int hq_vs = 0, hq_bs = 0;
+  minf::HeadTable ht{};
+  float scale = 0.f;
+};
+
+minf_status validate(const minf_problem* p, const minf_head_cfg* heads, Derived* d) {
+  g_err[0] = 0;
+  if (!p || !heads) return fail(MINF_EINVAL, "null problem or head table");
+  if (p->B < 1 || p->n < 1) return fail(MINF_EINVAL, "B and n must be >= 1 (B=%d n=%d)", p->B, p->n);
+  if (p->Hq < 1 || p->Hq > MINF_MAX_HEADS) return fail(MINF_EINVAL, "Hq must be in [1, %d] (Hq=%d)", MINF_MAX_HEADS, p->Hq);
+  if (p->Hkv < 1 || p->Hq % p->Hkv != 0) return fail(MINF_EINVAL, "Hq %% Hkv must be 0 (Hq=%d Hkv=%d)", p->Hq, p->Hkv);
+  if (p->dh != 64 && p->dh != 128) return fail(MINF_EUNSUPPORTED, "dh must be 64 or 128 (dh=%d)", p->dh);
+  if (p->in_dtype != MINF_F32 && p->in_dtype != MINF_BF16) return fail(MINF_EINVAL, "bad in_dtype %d", p->in_dtype);
+  if (p->out_dtype != MINF_F32 && p->out_dtype != MINF_BF16) return fail(MINF_EINVAL, "bad out_dtype %d", p->out_dtype);
+  if (!(p->scale >= 0.f) || isinf(p->scale)) return fail(MINF_EINVAL, "scale must be finite and >= 0");
+  if (p->block != MINF_BLOCK) return fail(MINF_EUNSUPPORTED, "block must be %d (block=%d)", MINF_BLOCK, p->block);
+  if (p->slash_tile == 1) return fail(MINF_EUNSUPPORTED, "slash_tile=1 (logical Eq. 5 slashes) is not implemented on the GPU");
+  if (p->slash_tile != 64) return fail(MINF_EINVAL, "slash_tile must be 64 (slash_tile=%d)", p->slash_tile);
+  if ((int64_t)p->B * p->Hq * p->n * p->dh > ((int64_t)1 << 40)) return fail(MINF_EINVAL, "problem too large");
+  d->nq = (p->n + MINF_BLOCK - 1) / MINF_BLOCK;
+  d->scale = p->scale > 0.f ? p->scale : 1.0f / sqrtf((float)p->dh);
+  int64_t mv = 0, ms = 0, mk = 0;
+  for (int h = 0; h < p->Hq; ++h) {
+    const minf_head_cfg& c = heads[h];
+    d->ht.kind[h] = c.kind;
+    switch (c.kind) {
+      case MINF_ASHAPE:
+        if (c.sink < 0 || c.window < 0) return fail(MINF_EINVAL, "head %d: A-shape sink/window must be >= 0", h);
+        d->ht.a[h] = (int32_t)std::min<int64_t>(c.sink, p->n);
+        d->ht.b[h] = (int32_t)std::min<int64_t>(c.window, p->n);
+        d->has_a = true;
+        break;
+      case MINF_VSLASH: {
+        if (c.last_q < 1 || c.last_q > MINF_MAX_LAST_Q)
+          return fail(c.last_q > MINF_MAX_LAST_Q ? MINF_EUNSUPPORTED : MINF_EINVAL,
+                      "head %d: last_q must be in [1, %d] (last_q=%d)", h, MINF_MAX_LAST_Q, c.last_q);
+        if (c.n_vertical < 0 || c.n_slash < 0) return fail(MINF_EINVAL, "head %d: negative VS budget", h);
+        const int64_t v = std::min<int64_t>(c.n_vertical, p->n), s = std::min<int64_t>(c.n_slash, p->n);
+        d->ht.a[h] = c.last_q;
+        d->ht.b[h] = (int32_t)v;
+        d->ht.c[h] = (int32_t)s;
+        mv = std::max(mv, v);
+        ms = std::max(ms, s);
+        d->has_vs = true;
+        d->hq_vs++;
+        break;
+      }
+      case MINF_BSPARSE: {
+        if (c.topk_blocks < 1) return fail(MINF_EINVAL, "head %d: topk_blocks must be >= 1", h);
+        if (c.force_flags & ~(MINF_FORCE_FIRST_BLOCK | MINF_FORCE_DIAG_BLOCK))
+          return fail(MINF_EINVAL, "head %d: unknown force flags 0x%x", h, c.force_flags);
+        const int64_t k = std::min<int64_t>(c.topk_blocks, d->nq);
+        d->ht.a[h] = (int32_t)k;
+        d->ht.b[h] = c.force_flags;
+        mk = std::max(mk, k);
+        d->has_bs = true;
+        d->hq_bs++;
+        break;
+      }
+      default:
+        return fail(MINF_EINVAL, "head %d: unknown pattern kind %d", h, c.kind);
+    }
+  }
+  d->max_v = round_up(mv, MINF_CHUNK);
+  d->max_s = std::max<int64_t>(ms, 1);
+  d->max_kb = std::max<int64_t>(mk, 1);
+  d->max_chunks = (p->n + 63 + 31) / 32 + d->max_s + 1;
+  d->bm_words = (p->n + 63 + 31) / 32;
+  return MINF_OK;
+}
+
+// ---- workspace layout (bytes, 256-aligned pieces) ----
+struct Carve {
+  size_t off = 0;
+  size_t take(size_t bytes) { size_t o = off; off += (bytes + 255) & ~size_t(255); return o; }
+};
+
+struct TilesWs { size_t span_cum, range_chunks, bitmap, head_ok, total; };
+TilesWs tiles_ws(const minf_problem* p, const Derived& d) {
+  Carve c;
+  TilesWs w;
+  const size_t BH = (size_t)p->B * p->Hq;
+  w.span_cum = c.take(BH * (d.max_s + 1) * 4);
+  w.range_chunks = c.take(BH * (d.max_s + 1) * 4);
+  w.bitmap = c.take(BH * d.bm_words * 4);
+  w.head_ok = c.take(BH * 4);
+  w.total = c.off;
+  return w;
+}
+
+// Block scores of at most this many bytes are resident at once; heads are
+// processed in batches that fit.
+constexpr size_t kScoreBytesCap = size_t(2) << 30;
+
+struct BsWs { size_t qbar, kbar, scores, total; int64_t score_heads; };
+BsWs bs_ws(const minf_problem* p, const Derived& d) {
+  Carve c;
+  BsWs w;
+  w.qbar = c.take((size_t)p->B * p->Hq * d.nq * p->dh * 4);
+  w.kbar = c.take((size_t)p->B * p->Hkv * d.nq * p->dh * 4);
+  const size_t per_head = (size_t)d.nq * d.nq * 4;
+  const int64_t heads = (int64_t)p->B * std::max(d.hq_bs, 1);
+  w.score_heads = std::max<int64_t>(1, std::min<int64_t>({heads, 64, (int64_t)(kScoreBytesCap / per_head)}));
+  w.scores = c.take(per_head * w.score_heads);
+  w.total = c.off;
+  return w;
+}
+
+minf::VsWs vs_ws(const minf_problem* p, const Derived& d) {
+  return minf::vs_workspace(p->B, p->Hq, p->n, (int)d.nq);
+}
+
+size_t ws_total(const minf_problem* p, const Derived& d) {
+  size_t t = tiles_ws(p, d).total;
+  if (d.has_bs) t = std::max(t, bs_ws(p, d).total);
+  if (d.has_vs) t = std::max(t, vs_ws(p, d).total);
+  return std::max<size_t>(t, 256);
+}
+
+minf_status check_ws(const minf_problem* p, const Derived& d, void* ws, size_t ws_bytes) {
+  const size_t need = ws_total(p, d);
+  if (!ws) return fail(MINF_EWORKSPACE, "workspace pointer is null");
+  if (ws_bytes < need) return fail(MINF_EWORKSPACE, "workspace of %zu bytes is smaller than the %zu needed", ws_bytes, need);
+  return MINF_OK;
+}
+
+minf_status hip_status(hipError_t e, const char* what) {
+  if (e == hipSuccess) return MINF_OK;
+  return fail(MINF_EHIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* minf_status_string(minf_status s) {
+  switch (s) {
+    case MINF_OK: return "ok";
+    case MINF_EINVAL: return "invalid argument";
+    case MINF_EUNSUPPORTED: return "unsupported";
+    case MINF_EWORKSPACE: return "workspace too small";
+    case MINF_ECAPACITY: return "capacity too small";
+    case MINF_EHIP: return "HIP error";
+  }
+  return "unknown status";
+}
+
+const char* minf_last_error(void) { return g_err; }
+const char* minf_version(void) { return "minf 0.1 gfx950"; }
+
+minf_status minf_query_sizes(const minf_problem* prob, const minf_head_cfg* heads, minf_sizes* out) {
+  Derived d;
+  minf_status s = validate(prob, heads, &d);
+  if (s != MINF_OK) return s;
+  if (!out) return fail(MINF_EINVAL, "null output");
+  out->nq = d.nq;
+  out->max_v = d.max_v;
+  out->max_s = d.max_s;
+  out->max_kb = d.max_kb;
+  out->max_chunks = d.max_chunks;
+  out->ws_bytes = (int64_t)ws_total(prob, d);
+  return MINF_OK;
+}
+
+minf_status minf_vs_index(const minf_problem* prob, const minf_head_cfg* heads, const void* Q, const void* K,
+                          int32_t* vert_idx, int32_t* slash_idx, float* vert_score, float* slash_score,
+                          void* ws, size_t ws_bytes, void* stream) {
+  Derived d;
+  minf_status s = validate(prob, heads, &d);
+  if (s != MINF_OK) return s;
+  if (!d.has_vs) return MINF_OK;
+  if (!Q || !K || !vert_idx || !slash_idx) return fail(MINF_EINVAL, "null Q, K or index output");
+  if ((s = check_ws(prob, d, ws, ws_bytes)) != MINF_OK) return s;
+  minf::VsParams v{};
+  v.Q = Q; v.K = K;
+  v.vert_idx = vert_idx; v.slash_idx = slash_idx;
+  v.vert_score = vert_score; v.slash_score = slash_score;
+  v.max_v = d.max_v; v.max_s = d.max_s;
+  v.B = prob->B; v.Hq = prob->Hq; v.Hkv = prob->Hkv; v.n = prob->n; v.dh = prob->dh;
+  v.in_bf16 = prob->in_dtype == MINF_BF16;
+  v.c = d.scale * minf::kLog2e;
+  v.ht = d.ht;
+  v.ws = vs_ws(prob, d);
+  v.ws_base = static_cast<char*>(ws);
+  return hip_status(minf::launch_vs_index(v, static_cast<hipStream_t>(stream)), "minf_vs_index launch");
+}
+
+minf_status minf_bs_index(const minf_problem* prob, const minf_head_cfg* heads, const void* Q, const void* K,
+                          int32_t* blk_idx, int32_t* blk_cnt, void* ws, size_t ws_bytes, void* stream) {
+  Derived d;
+  minf_status s = validate(prob, heads, &d);
+  if (s != MINF_OK) return s;
+  if (!d.has_bs) return MINF_OK;
+  if (!Q || !K || !blk_idx || !blk_cnt) return fail(MINF_EINVAL, "null Q, K or index output");
+  if ((s = check_ws(prob, d, ws, ws_bytes)) != MINF_OK) return s;
+  const BsWs w = bs_ws(prob, d);
+  minf::BsParams b{};
+  b.Q = Q; b.K = K; b.blk_idx = blk_idx; b.blk_cnt = blk_cnt;
+  b.qbar = reinterpret_cast<float*>(static_cast<char*>(ws) + w.qbar);
+  b.kbar = reinterpret_cast<float*>(static_cast<char*>(ws) + w.kbar);
+  b.scores = reinterpret_cast<float*>(static_cast<char*>(ws) + w.scores);
+  b.score_heads = w.score_heads;
+  b.max_kb = d.max_kb;
+  b.B = prob->B; b.Hq = prob->Hq; b.Hkv = prob->Hkv; b.n = prob->n; b.dh = prob->dh; b.nq = (int)d.nq;
+  b.in_bf16 = prob->in_dtype == MINF_BF16;
+  b.scale = d.scale;
+  b.ht = d.ht;
+  return hip_status(minf::launch_bs_index(b, static_cast<hipStream_t>(stream)), "minf_bs_index launch");
+}
+
+minf_status minf_build_tiles(const minf_problem* prob, const minf_head_cfg* heads, const int32_t* vert_idx,
+                             const int32_t* slash_idx, const int32_t* blk_idx, const int32_t* blk_cnt,
+                             const minf_tiles* tiles, void* ws, size_t ws_bytes, void* stream) {
+  Derived d;
+  minf_status s = validate(prob, heads, &d);
+  if (s != MINF_OK) return s;
+  if (!tiles || !tiles->kept_edges || !tiles->status) return fail(MINF_EINVAL, "null tiles, kept_edges or status");
+  if (d.has_vs && (!vert_idx || !slash_idx || !tiles->span_lo || !tiles->span_hi || !tiles->span_cnt ||
+                   !tiles->chunk_lo || !tiles->chunk_hi || !tiles->chunk_cnt || !tiles->cols || !tiles->col_cnt))
+    return fail(MINF_EINVAL, "a Vertical-Slash head needs vert_idx, slash_idx and every span/chunk/column buffer");
+  if (d.has_bs && (!blk_idx || !blk_cnt)) return fail(MINF_EINVAL, "a Block-Sparse head needs blk_idx and blk_cnt");
+  if ((s = check_ws(prob, d, ws, ws_bytes)) != MINF_OK) return s;
+  const TilesWs w = tiles_ws(prob, d);
+  char* base = static_cast<char*>(ws);
+  minf::TileParams t{};
+  t.vert_idx = vert_idx; t.slash_idx = slash_idx; t.blk_idx = blk_idx; t.blk_cnt = blk_cnt;
+  t.t = *tiles;
+  t.span_cum = reinterpret_cast<int32_t*>(base + w.span_cum);
+  t.range_chunks = reinterpret_cast<int32_t*>(base + w.range_chunks);
+  t.bitmap = reinterpret_cast<uint32_t*>(base + w.bitmap);
+  t.head_ok = reinterpret_cast<int32_t*>(base + w.head_ok);
+  t.max_v = d.max_v; t.max_s = d.max_s; t.max_kb = d.max_kb; t.max_chunks = d.max_chunks; t.bm_words = d.bm_words;
+  t.B = prob->B; t.Hq = prob->Hq; t.n = prob->n; t.nq = (int)d.nq;
+  t.ht = d.ht;
+  return hip_status(minf::launch_tiles(t, d.has_vs, d.has_bs, static_cast<hipStream_t>(stream)),
+                    "minf_build_tiles launch");
+}
+
+minf_status minf_sparse_attn(const minf_problem* prob, const minf_head_cfg* heads, const void* Q, const void* K,
+                             const void* V, const int32_t* blk_idx, const int32_t* blk_cnt, const minf_tiles* tiles,
+                             void* O, float* lse, void* ws, size_t ws_bytes, void* stream) {
+  Derived d;
+  minf_status s = validate(prob, heads, &d);
+  if (s != MINF_OK) return s;
+  (void)ws; (void)ws_bytes;
+  if (!Q || !K || !V || !O) return fail(MINF_EINVAL, "null Q, K, V or O");
+  if (d.has_bs && (!blk_idx || !blk_cnt)) return fail(MINF_EINVAL, "a Block-Sparse head needs blk_idx and blk_cnt");
+  if (d.has_vs && (!tiles || !tiles->chunk_lo || !tiles->chunk_hi || !tiles->chunk_cnt || !tiles->cols || !tiles->col_cnt))
+    return fail(MINF_EINVAL, "a Vertical-Slash head needs the tile lists from minf_build_tiles");
+  minf::AttnParams a{};
+  a.Q = Q; a.K = K; a.V = V; a.O = O; a.lse = lse;
+  a.blk_idx = blk_idx; a.blk_cnt = blk_cnt;
+  if (d.has_vs) {
+    a.chunk_lo = tiles->chunk_lo; a.chunk_hi = tiles->chunk_hi; a.chunk_cnt = tiles->chunk_cnt;
+    a.cols = tiles->cols; a.col_cnt = tiles->col_cnt;
+  }
+  a.max_kb = d.max_kb; a.max_chunks = d.max_chunks; a.max_v = d.max_v;
+  a.B = prob->B; a.Hq = prob->Hq; a.Hkv = prob->Hkv; a.n = prob->n; a.nq = (int)d.nq;
+  a.gsz = prob->Hq / prob->Hkv;
+  a.n_utiles = (int)((d.nq + 7) / 8);
+  a.n_segs = prob->B * a.n_utiles * prob->Hkv;
+  a.c = d.scale * minf::kLog2e;
+  a.out_bf16 = prob->out_dtype == MINF_BF16;
+  a.ht = d.ht;
+  return hip_status(minf::launch_attn(a, prob->in_dtype == MINF_BF16, prob->dh, static_cast<hipStream_t>(stream)),
+                    "minf_sparse_attn launch");
+}
+
+}  // extern "C"

@@ -1,0 +1,94 @@
+// Kernel parameter blocks and launchers shared between the host entry points
+// and the kernel translation units.
+#pragma once
+
+#include "common.h"
+
+namespace minf {
+
+// ---------------------------------------------------------------- attention
+struct AttnParams {
+  const void* Q;
+  const void* K;
+  const void* V;
+  void* O;
+  float* lse;
+  const int32_t* blk_idx;
+  const int32_t* blk_cnt;
+  const int32_t* chunk_lo;
+  const int32_t* chunk_hi;
+  const int32_t* chunk_cnt;
+  const int32_t* cols;
+  const int32_t* col_cnt;
+  int64_t max_kb, max_chunks, max_v;
+  int32_t B, Hq, Hkv, n, nq, gsz;
+  int32_t n_utiles, n_segs;
+  float c;          // scale * log2(e)
+  int32_t out_bf16;
+  HeadTable ht;     // ASHAPE: a = sink, b = window
+};
+hipError_t launch_attn(const AttnParams& p, int in_bf16, int dh, hipStream_t st);
+size_t attn_smem_bytes(int dh);
+
+// ---------------------------------------------------------------- tiles
+struct TileParams {
+  const int32_t* vert_idx;   // [B,Hq,max_v]
+  const int32_t* slash_idx;  // [B,Hq,max_s]
+  const int32_t* blk_idx;    // [B,Hq,nq,max_kb]
+  const int32_t* blk_cnt;    // [B,Hq,nq]
+  minf_tiles t;
+  int32_t* span_cum;         // ws [B,Hq,max_s+1]: covered offsets >= 0 before range r
+  int32_t* range_chunks;     // ws [B,Hq,max_s+1]: chunks before range r
+  uint32_t* bitmap;          // ws [B,Hq,bm_words]: bit x+63 set iff x in S
+  int32_t* head_ok;          // ws [B,Hq]
+  int64_t max_v, max_s, max_kb, max_chunks, bm_words;
+  int32_t B, Hq, n, nq;
+  HeadTable ht;              // ASHAPE: a = sink, b = window; VSLASH: b = #columns, c = #offsets
+};
+hipError_t launch_tiles(const TileParams& p, bool has_vs, bool has_bs, hipStream_t st);
+
+// ---------------------------------------------------------------- VS index
+constexpr int kVsWaveKeys = 256;                  // keys per wave in the proxy passes
+constexpr int kVsGroupKeys = 4 * kVsWaveKeys;     // keys per work-group
+constexpr int kVsDiagSlots = kVsWaveKeys + 64;    // diagonal partials per wave
+
+struct VsWs {
+  size_t part_m, part_l, lse2, cbuf, rbuf, dpart, total;
+  int64_t nslots;                                 // proxy waves per head
+};
+VsWs vs_workspace(int B, int Hq, int n, int nq);
+
+struct VsParams {
+  const void* Q;
+  const void* K;
+  int32_t* vert_idx;
+  int32_t* slash_idx;
+  float* vert_score;
+  float* slash_score;
+  int64_t max_v, max_s;
+  int32_t B, Hq, Hkv, n, dh, in_bf16;
+  float c;          // scale * log2(e)
+  HeadTable ht;     // VSLASH: a = last_q, b = #columns, c = #offsets
+  VsWs ws;
+  char* ws_base;
+};
+hipError_t launch_vs_index(const VsParams& p, hipStream_t st);
+
+// ---------------------------------------------------------------- BS index
+struct BsParams {
+  const void* Q;
+  const void* K;
+  int32_t* blk_idx;
+  int32_t* blk_cnt;
+  float* qbar;      // ws [B,Hq,nq,dh]
+  float* kbar;      // ws [B,Hkv,nq,dh]
+  float* scores;    // ws [heads in batch, nq, nq]
+  int64_t score_heads;   // heads whose score matrices fit the workspace at once
+  int64_t max_kb;
+  int32_t B, Hq, Hkv, n, dh, nq, in_bf16;
+  float scale;
+  HeadTable ht;     // BSPARSE: a = k_b (clipped to nq), b = force flags
+};
+hipError_t launch_bs_index(const BsParams& p, hipStream_t st);
+
+}  // namespace minf

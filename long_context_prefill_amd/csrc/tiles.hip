@@ -1,0 +1,287 @@
+// Index -> tile lists, and exact kept-edge counts.
+//
+// PaperTrace 2.1.2 "MInference", section 4.1 and blog-zz7 "LLM模型之MInference"
+// section 2.3.3 ("get Vertical-Slash index"): the selected slash offsets are
+// covered by square tiles (ranges), the verticals are points; ranges are
+// merged and a vertical that already lies inside a selected range is dropped
+// from the column list so that no (query, key) pair enters the softmax twice.
+//
+// Slash expansion used here: offset d covers, for query block u (64 rows), the
+// keys [64u - d, 64u + 63 - d].  Key j of block u is therefore covered iff
+// x = 64u - j lies in S = union over d of [d - 63, d].  S does not depend on
+// u, so the merged ranges of S are built once per head and every query block
+// reads them shifted by 64u.  The ranges are also cut into chunks of at most
+// 32 offsets (the attention kernel's unit of work); block u uses the chunks
+// whose lowest offset is <= 64u.
+//
+// Kept edges E_h = sum_i |N_h(i)| (section 1.2 of the page) are counted in
+// closed form per query block: slash keys through prefix counts of S, plus
+// the uncovered verticals, plus the block areas of Block-Sparse heads, plus
+// the A-shape formula sum_i min(i+1, g+w) (Eq. 4).
+#include "kernels.h"
+
+namespace minf {
+
+
+__device__ __forceinline__ int64_t ashape_edges(int64_t n, int64_t g, int64_t w) {
+  const int64_t m = g + w;       // |N(i)| = min(i+1, g+w)
+  if (n <= m) return n * (n + 1) / 2;
+  return m * (m + 1) / 2 + (n - m) * m;
+}
+
+// Block-wide exclusive scan of one int per thread (256 threads), returns the
+// total through *total.
+__device__ int block_exscan(int x, int* sh, int* total) {
+  const int t = threadIdx.x;
+  sh[t] = x;
+  __syncthreads();
+  for (int off = 1; off < 256; off <<= 1) {
+    int y = t >= off ? sh[t - off] : 0;
+    __syncthreads();
+    sh[t] += y;
+    __syncthreads();
+  }
+  const int incl = sh[t];
+  *total = sh[255];
+  __syncthreads();
+  return incl - x;
+}
+
+// 1) validate indices, initialise kept_edges, merge slash ranges.
+__global__ __launch_bounds__(256) void vs_ranges_kernel(TileParams P) {
+  __shared__ int sh[256];
+  __shared__ int bad_s, bad_v;
+  const int bh = blockIdx.x;
+  const int h = bh % P.Hq;
+  const int kind = P.ht.kind[h];
+  if (threadIdx.x == 0) {
+    int64_t e = 0;
+    if (kind == MINF_ASHAPE) e = ashape_edges(P.n, P.ht.a[h], P.ht.b[h]);
+    P.t.kept_edges[bh] = e;
+    bad_s = 0; bad_v = 0;
+  }
+  if (kind != MINF_VSLASH) return;
+  const int nv = P.ht.b[h], ns = P.ht.c[h];
+  const int32_t* offs = P.slash_idx + (size_t)bh * P.max_s;
+  const int32_t* cols = P.vert_idx + (size_t)bh * P.max_v;
+  __syncthreads();
+  for (int k = threadIdx.x; k < ns; k += 256) {
+    const int d = offs[k];
+    if (d < 0 || d >= P.n || (k > 0 && offs[k - 1] >= d)) bad_s = 1;
+  }
+  for (int k = threadIdx.x; k < nv; k += 256) {
+    const int c = cols[k];
+    if (c < 0 || c >= P.n || (k > 0 && cols[k - 1] >= c)) bad_v = 1;
+  }
+  __syncthreads();
+  const bool ok = !(bad_s || bad_v);
+  if (threadIdx.x == 0) {
+    P.head_ok[bh] = ok ? 1 : 0;
+    if (!ok) atomicOr(P.t.status, (bad_s ? MINF_DEV_BAD_SLASH : 0) | (bad_v ? MINF_DEV_BAD_VERTICAL : 0));
+  }
+  int carry = 0;   // ranges emitted so far
+  if (ok) {
+    for (int base = 0; base < ns; base += 256) {
+      const int k = base + threadIdx.x;
+      int flag = 0, d = 0;
+      if (k < ns) {
+        d = offs[k];
+        flag = (k == 0) || (d - offs[k - 1] > 64);
+      }
+      int tot;
+      const int pos = carry + block_exscan(flag, sh, &tot);   // index of the new range if flag
+      if (k < ns) {
+        if (flag) P.t.span_lo[(size_t)bh * P.max_s + pos] = d - 63;
+        const bool last = (k == ns - 1) || (offs[k + 1] - d > 64);
+        if (last) P.t.span_hi[(size_t)bh * P.max_s + pos + flag - 1] = d;
+      }
+      carry += tot;
+    }
+  }
+  if (threadIdx.x == 0) P.t.span_cnt[bh] = ok ? carry : 0;
+}
+
+// 2) cut ranges into chunks, prefix counts, coverage bitmap.
+__global__ __launch_bounds__(256) void vs_chunks_kernel(TileParams P) {
+  __shared__ int sh[256];
+  const int bh = blockIdx.x;
+  const int h = bh % P.Hq;
+  if (P.ht.kind[h] != MINF_VSLASH) return;
+  const int nr = P.t.span_cnt[bh];
+  const int32_t* lo = P.t.span_lo + (size_t)bh * P.max_s;
+  const int32_t* hi = P.t.span_hi + (size_t)bh * P.max_s;
+  int32_t* cum = P.span_cum + (size_t)bh * (P.max_s + 1);
+  int32_t* rch = P.range_chunks + (size_t)bh * (P.max_s + 1);
+  int carry_c = 0, carry_x = 0;
+  for (int base = 0; base < nr; base += 256) {
+    const int r = base + threadIdx.x;
+    int nch = 0, cov = 0, a = 0, bb = 0;
+    if (r < nr) {
+      a = lo[r]; bb = hi[r];
+      nch = (bb - a + 32) >> 5;
+      cov = bb >= 0 ? bb - max(a, 0) + 1 : 0;
+    }
+    int tc, tx;
+    const int pc = carry_c + block_exscan(nch, sh, &tc);
+    const int px = carry_x + block_exscan(cov, sh, &tx);
+    if (r < nr) {
+      rch[r] = pc;
+      cum[r] = px;
+    }
+    carry_c += tc;
+    carry_x += tx;
+  }
+  if (threadIdx.x == 0) { rch[nr] = carry_c; cum[nr] = carry_x; }
+  if (threadIdx.x == 0 && carry_c > P.max_chunks) atomicOr(P.t.status, MINF_DEV_CAPACITY);
+  __syncthreads();
+  // chunk c belongs to the range r with rch[r] <= c < rch[r+1]
+  const int nchunks = min<long long>(carry_c, P.max_chunks);
+  for (int c = threadIdx.x; c < nchunks; c += 256) {
+    int l = 0, rr = nr;   // last r with rch[r] <= c
+    while (rr - l > 1) { const int mid = (l + rr) >> 1; if (rch[mid] <= c) l = mid; else rr = mid; }
+    const int m = c - rch[l];
+    P.t.chunk_lo[(size_t)bh * P.max_chunks + c] = lo[l] + 32 * m;
+    P.t.chunk_hi[(size_t)bh * P.max_chunks + c] = min(lo[l] + 32 * m + 31, hi[l]);
+  }
+  // coverage bitmap over x in [-63, n): bit (x + 63)
+  uint32_t* bm = P.bitmap + (size_t)bh * P.bm_words;
+  for (int w = threadIdx.x; w < P.bm_words; w += 256) {
+    const int x0 = 32 * w - 63, x1 = x0 + 31;
+    // first range with hi >= x0
+    int l = 0, rr = nr;
+    while (l < rr) { const int mid = (l + rr) >> 1; if (hi[mid] < x0) l = mid + 1; else rr = mid; }
+    uint32_t bits = 0;
+    for (int r = l; r < nr && lo[r] <= x1; ++r) {
+      const int s = max(lo[r], x0) - x0, e = min(hi[r], x1) - x0;
+      const uint32_t span = (e - s + 1 == 32) ? 0xffffffffu : (((1u << (e - s + 1)) - 1u) << s);
+      bits |= span;
+    }
+    bm[w] = bits;
+  }
+}
+
+__device__ __forceinline__ bool covered(const uint32_t* bm, int x) {
+  const int i = x + 63;
+  return (bm[i >> 5] >> (i & 31)) & 1u;
+}
+
+// 3) per query block: chunk count, uncovered verticals, kept edges (VS).
+//    One wave per query block.
+__global__ __launch_bounds__(256) void vs_cols_kernel(TileParams P) {
+  const int bh = blockIdx.y;
+  const int h = bh % P.Hq;
+  if (P.ht.kind[h] != MINF_VSLASH) return;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int u = blockIdx.x * 4 + wave;
+  __shared__ unsigned long long part[4];
+  unsigned long long edges = 0;
+  if (u < P.nq) {
+    const int row0 = 64 * u;
+    const int Lu = min(64, P.n - row0);
+    const int row_end = row0 + Lu - 1;
+    const size_t bu = (size_t)bh * P.nq + u;
+    const bool ok = P.head_ok[bh] != 0;
+    const int nr = ok ? P.t.span_cnt[bh] : 0;
+    const int32_t* lo = P.t.span_lo + (size_t)bh * P.max_s;
+    const int32_t* hi = P.t.span_hi + (size_t)bh * P.max_s;
+    const int32_t* cum = P.span_cum + (size_t)bh * (P.max_s + 1);
+    const int32_t* rch = P.range_chunks + (size_t)bh * (P.max_s + 1);
+    const uint32_t* bm = P.bitmap + (size_t)bh * P.bm_words;
+    // last range with lo <= 64u
+    const int X = row0;
+    int l = 0, r = nr;
+    while (l < r) { const int mid = (l + r) >> 1; if (lo[mid] <= X) l = mid + 1; else r = mid; }
+    const int rs = l - 1;   // -1 if none
+    int ccnt = 0;
+    long long cov_pos = 0;  // |S intersect [0, X]|
+    if (rs >= 0) {
+      ccnt = rch[rs] + min((hi[rs] - lo[rs] + 32) >> 5, ((X - lo[rs]) >> 5) + 1);
+      const int e = min(hi[rs], X), s = max(lo[rs], 0);
+      cov_pos = cum[rs] + (e >= s ? e - s + 1 : 0);
+    }
+    ccnt = min<long long>(ccnt, P.max_chunks);
+    // span edges: Lu per covered x >= 0 with x <= 64u, and max(0, Lu + x) for x in [-63, -1]
+    if (lane == 0) {
+      long long e = (long long)Lu * cov_pos;
+      if (nr > 0) {
+        for (int x = -63; x <= -1; ++x)
+          if (Lu + x > 0 && covered(bm, x)) e += Lu + x;
+      }
+      edges += e;
+      P.t.chunk_cnt[bu] = ccnt;
+    }
+    // uncovered verticals of this block, ascending
+    const int nv = ok ? P.ht.b[h] : 0;
+    const int32_t* cols = P.vert_idx + (size_t)bh * P.max_v;
+    int32_t* out = P.t.cols + bu * P.max_v;
+    int cnt = 0;
+    for (int base = 0; base < nv; base += 64) {
+      const int k = base + lane;
+      const int c = k < nv ? cols[k] : 0x7fffffff;
+      const bool in_range = c <= row_end;
+      const bool keep = in_range && !covered(bm, row0 - c);
+      const unsigned long long m = __ballot(keep);
+      const int pos = cnt + __popcll(m & ((1ull << lane) - 1ull));
+      if (keep) {
+        out[pos] = c;
+        edges += row_end - max(c, row0) + 1;
+      }
+      cnt += __popcll(m);
+      if (__any(!in_range)) break;   // columns are ascending: the rest lie beyond the block
+    }
+    if (lane == 0) P.t.col_cnt[bu] = cnt;
+  }
+  // reduce edges over the work-group, one atomic per group (integer: order-free)
+  for (int off = 32; off > 0; off >>= 1) edges += __shfl_xor(edges, off);
+  if (lane == 0) part[wave] = edges;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const unsigned long long tot = part[0] + part[1] + part[2] + part[3];
+    if (tot) atomicAdd(reinterpret_cast<unsigned long long*>(P.t.kept_edges + bh), tot);
+  }
+}
+
+// 4) Block-Sparse: validate J_u and count the kept block areas.
+__global__ __launch_bounds__(256) void bs_edges_kernel(TileParams P) {
+  const int bh = blockIdx.y;
+  const int h = bh % P.Hq;
+  if (P.ht.kind[h] != MINF_BSPARSE) return;
+  const int u = blockIdx.x * 256 + threadIdx.x;
+  __shared__ unsigned long long part[4];
+  unsigned long long edges = 0;
+  if (u < P.nq) {
+    const size_t bu = (size_t)bh * P.nq + u;
+    const int cnt = P.blk_cnt[bu];
+    const int Lu = min(64, P.n - 64 * u);
+    bool bad = cnt < 0 || cnt > P.max_kb || cnt > u + 1;
+    const int32_t* J = P.blk_idx + bu * P.max_kb;
+    int prev = -1;
+    for (int i = 0; !bad && i < cnt; ++i) {
+      const int v = J[i];
+      if (v <= prev || v > u) { bad = true; break; }
+      edges += (v < u) ? (unsigned long long)Lu * 64ull : (unsigned long long)(Lu * (Lu + 1) / 2);
+      prev = v;
+    }
+    if (bad) { atomicOr(P.t.status, MINF_DEV_BAD_BLOCK); edges = 0; }
+  }
+  for (int off = 32; off > 0; off >>= 1) edges += __shfl_xor(edges, off);
+  if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = edges;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const unsigned long long tot = part[0] + part[1] + part[2] + part[3];
+    if (tot) atomicAdd(reinterpret_cast<unsigned long long*>(P.t.kept_edges + bh), tot);
+  }
+}
+
+hipError_t launch_tiles(const TileParams& p, bool has_vs, bool has_bs, hipStream_t st) {
+  const unsigned BH = (unsigned)(p.B * p.Hq);
+  hipLaunchKernelGGL(vs_ranges_kernel, dim3(BH), dim3(256), 0, st, p);
+  if (has_vs) {
+    hipLaunchKernelGGL(vs_chunks_kernel, dim3(BH), dim3(256), 0, st, p);
+    hipLaunchKernelGGL(vs_cols_kernel, dim3((p.nq + 3) / 4, BH), dim3(256), 0, st, p);
+  }
+  if (has_bs) hipLaunchKernelGGL(bs_edges_kernel, dim3((p.nq + 255) / 256, BH), dim3(256), 0, st, p);
+  return hipGetLastError();
+}
+
+}  // namespace minf

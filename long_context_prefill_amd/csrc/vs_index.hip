@@ -1,0 +1,342 @@
+// Vertical-Slash index estimation.
+//
+// PaperTrace 2.1.2 "MInference", section 6.2 (estimating columns and offsets
+// from sampled queries) and blog-zz7 "LLM模型之MInference" section 2.3.2 (the
+// last queries against all keys): for each VS head h and its last
+// L = min(last_q, n) rows i, the proxy weights are the causal softmax
+//   a_ij = exp(s_ij - LSE_i),  s_ij = scale * q_i . k_j,  j <= i,
+// the column score is c_j = sum_i a_ij and the slash score r_d = sum_i a_{i,i-d};
+// the top-v columns and the top-s offsets are kept.
+//
+// GPU plan:
+//  pass 1  every wave takes 256 consecutive keys, forms S^T = K . Q^T for the
+//          64 sampled rows with the bf16 (or fp32) matrix cores and keeps a
+//          running (max, sum) per row -> per-wave partials;
+//  lse     the partials of each row are combined in a fixed order;
+//  pass 2  the same S^T tiles are recomputed and turned into exact
+//          probabilities; column sums are finished inside the wave (every key
+//          belongs to exactly one wave) and diagonal sums are accumulated per
+//          wave through a small LDS tile, then written as partials;
+//  diag    each offset's two neighbouring partials are added in a fixed order;
+//  top-k   exact radix select per (head, score array).
+// No floating-point atomics are used, so two runs give identical bits.
+#include <type_traits>
+
+#include "kernels.h"
+#include "topk.h"
+
+namespace minf {
+
+VsWs vs_workspace(int B, int Hq, int n, int nq) {
+  (void)nq;
+  VsWs w{};
+  const int64_t BH = (int64_t)B * Hq;
+  w.nslots = ((int64_t)n + kVsGroupKeys - 1) / kVsGroupKeys * 4;
+  size_t off = 0;
+  auto take = [&](size_t bytes) { size_t o = off; off += (bytes + 255) & ~size_t(255); return o; };
+  w.part_m = take(BH * 64 * w.nslots * 4);
+  w.part_l = take(BH * 64 * w.nslots * 4);
+  w.lse2 = take(BH * 64 * 4);
+  w.cbuf = take(BH * (size_t)n * 4);
+  w.rbuf = take(BH * (size_t)n * 4);
+  w.dpart = take(BH * w.nslots * kVsDiagSlots * 4);
+  w.total = off;
+  return w;
+}
+
+namespace {
+
+template <typename T, int DH>
+struct ProxyOps {
+  static constexpr int KS = (sizeof(T) == 2) ? DH / 32 : DH / 4;
+  using QOp = typename std::conditional<(sizeof(T) == 2), u32x4, float>::type;
+
+  // A operand (keys) for 16 keys starting at `key0 + 16*hh`: lane row r16.
+  __device__ static __forceinline__ void load_k(const T* Kb, int key, int g, QOp (&k)[KS]) {
+    if constexpr (sizeof(T) == 2) {
+      const u32x4* p = reinterpret_cast<const u32x4*>(Kb + (size_t)key * DH + g * (DH / 4));
+      #pragma unroll
+      for (int s = 0; s < KS; ++s) k[s] = p[s];
+    } else {
+      const floatx4* p = reinterpret_cast<const floatx4*>(Kb + (size_t)key * DH + g * (DH / 4));
+      #pragma unroll
+      for (int s = 0; s < KS / 4; ++s) {
+        floatx4 x = p[s];
+        k[4 * s] = x[0]; k[4 * s + 1] = x[1]; k[4 * s + 2] = x[2]; k[4 * s + 3] = x[3];
+      }
+    }
+  }
+  __device__ static __forceinline__ void zero(QOp (&q)[KS]) {
+    #pragma unroll
+    for (int s = 0; s < KS; ++s) {
+      if constexpr (sizeof(T) == 2) q[s] = u32x4{0, 0, 0, 0};
+      else q[s] = 0.f;
+    }
+  }
+  __device__ static __forceinline__ floatx4 dot(const QOp (&k)[KS], const QOp (&q)[KS]) {
+    floatx4 a = {0.f, 0.f, 0.f, 0.f};
+    #pragma unroll
+    for (int s = 0; s < KS; ++s) {
+      if constexpr (sizeof(T) == 2) a = mma_bf16(k[s], q[s], a);
+      else a = mma_f32(k[s], q[s], a);
+    }
+    return a;
+  }
+};
+
+// PASS 1: per-row running (max, sum) partials.  PASS 2: probabilities,
+// column sums and diagonal partials.
+template <typename T, int DH, int PASS>
+__global__ __launch_bounds__(256) void vs_proxy_kernel(VsParams P) {
+  using Ops = ProxyOps<T, DH>;
+  const int bh = blockIdx.y;
+  const int h = bh % P.Hq;
+  if (P.ht.kind[h] != MINF_VSLASH) return;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int r16 = lane & 15, g = lane >> 4;
+  const int n = P.n;
+  const int L = min(P.ht.a[h], n);
+  const int gsz = P.Hq / P.Hkv;
+  const int b = bh / P.Hq;
+  const int kv = h / gsz;
+  const T* Qb = reinterpret_cast<const T*>(P.Q) + (size_t)bh * n * DH;
+  const T* Kb = reinterpret_cast<const T*>(P.K) + ((size_t)b * P.Hkv + kv) * n * DH;
+  const int slot = blockIdx.x * 4 + wave;
+  const int J0 = slot * kVsWaveKeys;
+  const int J1 = min(J0 + kVsWaveKeys, n);
+  const int row_base = n - L;    // sampled row r is query n - L + r (valid for r < L)
+
+  typename Ops::QOp q[4][Ops::KS];
+  #pragma unroll
+  for (int nb = 0; nb < 4; ++nb) {
+    const int r = 16 * nb + r16;
+    if (r < L) Ops::load_k(Qb, row_base + r, g, q[nb]);
+    else Ops::zero(q[nb]);
+  }
+
+  float m_run[4], l_run[4], lse2[4];
+  #pragma unroll
+  for (int nb = 0; nb < 4; ++nb) { m_run[nb] = kNegInf; l_run[nb] = 0.f; lse2[nb] = 0.f; }
+  float* cdst = P.vert_score ? P.vert_score : reinterpret_cast<float*>(P.ws_base + P.ws.cbuf);
+  cdst += (size_t)bh * n;
+  float dslot[5] = {0.f, 0.f, 0.f, 0.f, 0.f};
+  __shared__ float ptile[4][64][33];
+  if constexpr (PASS == 2) {
+    const float* l2 = reinterpret_cast<const float*>(P.ws_base + P.ws.lse2) + (size_t)bh * 64;
+    #pragma unroll
+    for (int nb = 0; nb < 4; ++nb) lse2[nb] = l2[16 * nb + r16];
+  }
+
+  for (int j = J0, step = 0; j < J1; j += 32, ++step) {
+    typename Ops::QOp kop[2][Ops::KS];
+    #pragma unroll
+    for (int hh = 0; hh < 2; ++hh) Ops::load_k(Kb, min(j + 16 * hh + r16, n - 1), g, kop[hh]);
+    floatx4 s[2][4];
+    #pragma unroll
+    for (int hh = 0; hh < 2; ++hh)
+      #pragma unroll
+      for (int nb = 0; nb < 4; ++nb) s[hh][nb] = Ops::dot(kop[hh], q[nb]);
+    // valid pairs: sampled row r < L, key < n, key <= query index
+    const bool need_mask = (L < 64) || (j + 31 > row_base);
+    if (need_mask) {
+      #pragma unroll
+      for (int nb = 0; nb < 4; ++nb) {
+        const int r = 16 * nb + r16;
+        #pragma unroll
+        for (int hh = 0; hh < 2; ++hh)
+          #pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int key = j + 16 * hh + 4 * g + i;
+            if (!(r < L && key < n && key <= row_base + r)) s[hh][nb][i] = kNegInf;
+          }
+      }
+    }
+    if constexpr (PASS == 1) {
+      #pragma unroll
+      for (int nb = 0; nb < 4; ++nb) {
+        float x = fmaxf(fmaxf(fmaxf(s[0][nb][0], s[0][nb][1]), fmaxf(s[0][nb][2], s[0][nb][3])),
+                        fmaxf(fmaxf(s[1][nb][0], s[1][nb][1]), fmaxf(s[1][nb][2], s[1][nb][3])));
+        x = fmaxf(x, __shfl_xor(x, 16));
+        x = fmaxf(x, __shfl_xor(x, 32));
+        x *= P.c;
+        if (x > m_run[nb]) {
+          l_run[nb] *= fast_exp2(m_run[nb] - x);   // m_run = -inf gives 0
+          m_run[nb] = x;
+        }
+        const float msub = (m_run[nb] == kNegInf) ? 0.f : m_run[nb];
+        float ls = 0.f;
+        #pragma unroll
+        for (int hh = 0; hh < 2; ++hh)
+          #pragma unroll
+          for (int i = 0; i < 4; ++i) ls += fast_exp2(__builtin_fmaf(s[hh][nb][i], P.c, -msub));
+        l_run[nb] += ls;
+      }
+    } else {
+      float p[2][4][4];
+      #pragma unroll
+      for (int nb = 0; nb < 4; ++nb)
+        #pragma unroll
+        for (int hh = 0; hh < 2; ++hh)
+          #pragma unroll
+          for (int i = 0; i < 4; ++i) p[hh][nb][i] = fast_exp2(__builtin_fmaf(s[hh][nb][i], P.c, -lse2[nb]));
+      // column sums: over the 4 row groups in the lane, then over the 16 lanes of the row group
+      float cs[2][4];
+      #pragma unroll
+      for (int hh = 0; hh < 2; ++hh)
+        #pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          float x = (p[hh][0][i] + p[hh][1][i]) + (p[hh][2][i] + p[hh][3][i]);
+          x += __shfl_xor(x, 1);
+          x += __shfl_xor(x, 2);
+          x += __shfl_xor(x, 4);
+          x += __shfl_xor(x, 8);
+          cs[hh][i] = x;
+        }
+      // lane r16 < 8 writes key 16*(r16/4) + 4g + r16%4
+      if (r16 < 8) {
+        const int hh = r16 >> 2, i = r16 & 3;
+        float val = 0.f;
+        #pragma unroll
+        for (int a = 0; a < 2; ++a)
+          #pragma unroll
+          for (int bq = 0; bq < 4; ++bq)
+            if (a == hh && bq == i) val = cs[a][bq];
+        const int key = j + 16 * hh + 4 * g + i;
+        if (key < n) cdst[key] = val;
+      }
+      // diagonal partials: tile[r][jl] = p(row r, key j + jl)
+      #pragma unroll
+      for (int nb = 0; nb < 4; ++nb)
+        #pragma unroll
+        for (int hh = 0; hh < 2; ++hh)
+          #pragma unroll
+          for (int i = 0; i < 4; ++i) ptile[wave][16 * nb + r16][16 * hh + 4 * g + i] = p[hh][nb][i];
+      // the tile is private to this wave: LDS accesses of one wave complete in
+      // issue order, so a wave-scope fence (no work-group barrier: waves of a
+      // group may run different trip counts) orders the writes before the reads
+      __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      // slot t (d = dbase + t) of this wave's 320 owns diagonal x = t - 255 + 32*step
+      #pragma unroll
+      for (int qd = 0; qd < 5; ++qd) {
+        const int t = lane + 64 * qd;
+        const int x = t - (kVsWaveKeys - 1) + 32 * step;
+        if (x >= -31 && x <= 63) {
+          float acc = 0.f;
+          const int r0 = max(0, x), r1 = min(64, x + 32);
+          for (int r = r0; r < r1; ++r) acc += ptile[wave][r][r - x];
+          dslot[qd] += acc;
+        }
+      }
+      __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+    }
+  }
+
+  if constexpr (PASS == 1) {
+    #pragma unroll
+    for (int nb = 0; nb < 4; ++nb) {
+      l_run[nb] += __shfl_xor(l_run[nb], 16);
+      l_run[nb] += __shfl_xor(l_run[nb], 32);
+    }
+    if (g == 0) {
+      float* pm = reinterpret_cast<float*>(P.ws_base + P.ws.part_m) + (size_t)bh * 64 * P.ws.nslots;
+      float* pl = reinterpret_cast<float*>(P.ws_base + P.ws.part_l) + (size_t)bh * 64 * P.ws.nslots;
+      #pragma unroll
+      for (int nb = 0; nb < 4; ++nb) {
+        const int r = 16 * nb + r16;
+        pm[(size_t)r * P.ws.nslots + slot] = m_run[nb];
+        pl[(size_t)r * P.ws.nslots + slot] = l_run[nb];
+      }
+    }
+  } else {
+    float* dp = reinterpret_cast<float*>(P.ws_base + P.ws.dpart) + ((size_t)bh * P.ws.nslots + slot) * kVsDiagSlots;
+    #pragma unroll
+    for (int qd = 0; qd < 5; ++qd) dp[lane + 64 * qd] = dslot[qd];
+  }
+}
+
+// LSE of every sampled row from the per-wave partials (fixed order).
+__global__ __launch_bounds__(64) void vs_lse_kernel(VsParams P, int nslots_used) {
+  const int bh = blockIdx.x;
+  const int h = bh % P.Hq;
+  if (P.ht.kind[h] != MINF_VSLASH) return;
+  const int r = threadIdx.x;
+  const float* pm = reinterpret_cast<const float*>(P.ws_base + P.ws.part_m) + ((size_t)bh * 64 + r) * P.ws.nslots;
+  const float* pl = reinterpret_cast<const float*>(P.ws_base + P.ws.part_l) + ((size_t)bh * 64 + r) * P.ws.nslots;
+  float M = kNegInf;
+  for (int s = 0; s < nslots_used; ++s) M = fmaxf(M, pm[s]);
+  float Lsum = 0.f;
+  if (M != kNegInf)
+    for (int s = 0; s < nslots_used; ++s) Lsum += fast_exp2(pm[s] - M) * pl[s];
+  float* l2 = reinterpret_cast<float*>(P.ws_base + P.ws.lse2) + (size_t)bh * 64;
+  // rows without any key (r >= L) get +inf so that their probabilities are 0
+  l2[r] = (Lsum > 0.f) ? M + __log2f(Lsum) : __builtin_huge_valf();
+}
+
+// r_d = sum of the (at most two) wave partials whose keys can form offset d.
+__global__ __launch_bounds__(256) void vs_diag_kernel(VsParams P) {
+  const int bh = blockIdx.y;
+  const int h = bh % P.Hq;
+  if (P.ht.kind[h] != MINF_VSLASH) return;
+  const int n = P.n;
+  const int L = min(P.ht.a[h], n);
+  const int d = blockIdx.x * 256 + threadIdx.x;
+  if (d >= n) return;
+  const float* dp = reinterpret_cast<const float*>(P.ws_base + P.ws.dpart) + (size_t)bh * P.ws.nslots * kVsDiagSlots;
+  const int jlo = max(0, n - L - d), jhi = n - 1 - d;
+  const int w1 = jlo / kVsWaveKeys, w2 = jhi / kVsWaveKeys;
+  float acc = 0.f;
+  for (int w = w1; w <= w2; ++w) {
+    const int dbase = n - L - w * kVsWaveKeys - (kVsWaveKeys - 1);
+    acc += dp[(size_t)w * kVsDiagSlots + (d - dbase)];
+  }
+  float* rdst = P.slash_score ? P.slash_score : reinterpret_cast<float*>(P.ws_base + P.ws.rbuf);
+  rdst[(size_t)bh * n + d] = acc;
+}
+
+// Top-v columns / top-s offsets, one work-group per (head, array).
+__global__ __launch_bounds__(1024) void vs_topk_kernel(VsParams P) {
+  const int bh = blockIdx.x >> 1;
+  const int which = blockIdx.x & 1;
+  const int h = bh % P.Hq;
+  if (P.ht.kind[h] != MINF_VSLASH) return;
+  __shared__ TopkShared sh;
+  const int n = P.n;
+  const float* src;
+  int32_t* out;
+  int k, cap;
+  if (which == 0) {
+    src = (P.vert_score ? P.vert_score : reinterpret_cast<const float*>(P.ws_base + P.ws.cbuf)) + (size_t)bh * n;
+    out = P.vert_idx + (size_t)bh * P.max_v;
+    k = P.ht.b[h];
+    cap = (int)P.max_v;
+  } else {
+    src = (P.slash_score ? P.slash_score : reinterpret_cast<const float*>(P.ws_base + P.ws.rbuf)) + (size_t)bh * n;
+    out = P.slash_idx + (size_t)bh * P.max_s;
+    k = P.ht.c[h];
+    cap = (int)P.max_s;
+  }
+  block_topk<1024, 16>([&](int i) { return src[i]; }, n, k, out, cap, sh);
+}
+
+template <typename T, int DH>
+hipError_t launch_t(const VsParams& p, hipStream_t st) {
+  const unsigned BH = (unsigned)(p.B * p.Hq);
+  const unsigned nwg = (unsigned)((p.n + kVsGroupKeys - 1) / kVsGroupKeys);
+  hipLaunchKernelGGL((vs_proxy_kernel<T, DH, 1>), dim3(nwg, BH), dim3(256), 0, st, p);
+  hipLaunchKernelGGL(vs_lse_kernel, dim3(BH), dim3(64), 0, st, p, (int)(nwg * 4));
+  hipLaunchKernelGGL((vs_proxy_kernel<T, DH, 2>), dim3(nwg, BH), dim3(256), 0, st, p);
+  hipLaunchKernelGGL(vs_diag_kernel, dim3((p.n + 255) / 256, BH), dim3(256), 0, st, p);
+  hipLaunchKernelGGL(vs_topk_kernel, dim3(2 * BH), dim3(1024), 0, st, p);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_vs_index(const VsParams& p, hipStream_t st) {
+  if (p.in_bf16) return p.dh == 128 ? launch_t<uint16_t, 128>(p, st) : launch_t<uint16_t, 64>(p, st);
+  return p.dh == 128 ? launch_t<float, 128>(p, st) : launch_t<float, 64>(p, st);
+}
+
+}  // namespace minf

@@ -1,0 +1,142 @@
+"""Helpers shared by the GPU parity tests (not collected as tests).
+
+Moves seeded problems to the device, feeds the oracle's index sets to the
+GPU path, and compares results with the oracle element by element.
+"""
+import math
+import sys
+import time
+
+import numpy as np
+
+import long_context_prefill_amd as M
+from oracle import minf_oracle as O
+
+BF16_MAX_ABS, BF16_MEAN_ABS = 1e-2, 1e-3
+F32_MAX_ABS, F32_MEAN_ABS = 1e-5, 1e-5
+NEAR_TIE_REL = 1e-4
+
+
+def log(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def device_inputs(p, device="cuda"):
+    import torch
+    if p.dtype == "bf16":
+        conv = lambda x: torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).to(device)
+    else:
+        conv = lambda x: torch.from_numpy(np.ascontiguousarray(x)).to(device)
+    return conv(p.Q), conv(p.K), conv(p.V)
+
+
+def make_prob(p, out_dtype="f32"):
+    return M.make_problem(p.B, p.Hq, p.Hkv, p.n, p.dh, p.dtype, out_dtype, p.scale)
+
+
+def load_oracle_indices(p, res, buf):
+    """Write the oracle's VS / BS index sets into the GPU index buffers."""
+    import torch
+    sz = buf["sizes"]
+    B, Hq, nq = p.B, p.Hq, int(sz.nq)
+    vi = np.full((B, Hq, int(sz.max_v) or 1), -1, np.int32)
+    si = np.full((B, Hq, int(sz.max_s)), -1, np.int32)
+    bi = np.full((B, Hq, nq, int(sz.max_kb)), -1, np.int32)
+    bc = np.zeros((B, Hq, nq), np.int32)
+    for (b, h), r in res["heads"].items():
+        if r.kind == O.VSLASH:
+            vi[b, h, :len(r.cols)] = r.cols
+            si[b, h, :len(r.offs)] = r.offs
+        elif r.kind == O.BSPARSE:
+            for u, J in enumerate(r.J):
+                bi[b, h, u, :len(J)] = J
+                bc[b, h, u] = len(J)
+    dev = buf["vert_idx"].device
+    buf["vert_idx"].copy_(torch.from_numpy(vi).to(dev))
+    buf["slash_idx"].copy_(torch.from_numpy(si).to(dev))
+    buf["blk_idx"].copy_(torch.from_numpy(bi).to(dev))
+    buf["blk_cnt"].copy_(torch.from_numpy(bc).to(dev))
+
+
+def compare_output(O_gpu, O_ref, dtype, what=""):
+    """Element-wise comparison to the benchmark spec's tolerances."""
+    d = np.abs(np.asarray(O_gpu, dtype=np.float64) - O_ref)
+    mx, mean = float(d.max()) if d.size else 0.0, float(d.mean()) if d.size else 0.0
+    lim = (BF16_MAX_ABS, BF16_MEAN_ABS) if dtype == "bf16" else (F32_MAX_ABS, F32_MEAN_ABS)
+    log(f"  {what}: max-abs {mx:.3e} (<= {lim[0]:g}), mean-abs {mean:.3e} (<= {lim[1]:g})")
+    assert np.all(np.isfinite(O_gpu)), f"{what}: non-finite output"
+    assert mx <= lim[0], f"{what}: max-abs {mx} > {lim[0]}"
+    assert mean <= lim[1], f"{what}: mean-abs {mean} > {lim[1]}"
+    return mx, mean
+
+
+def check_selection(gpu_idx, scores, k, what):
+    """GPU top-k vs the oracle's: identical except candidates whose oracle
+    score lies within 1e-4 relative of the k-th threshold.  Returns
+    (number of differences, number exempt)."""
+    g = np.asarray(gpu_idx, dtype=np.int64)
+    g = g[g >= 0]
+    k = min(int(k), scores.shape[0])
+    assert g.shape[0] == k, f"{what}: {g.shape[0]} indices, expected {k}"
+    assert np.all(np.diff(g) > 0), f"{what}: not strictly ascending"
+    ref = O.topk_ascending(scores, k)
+    if k == 0:
+        return 0, 0
+    t = O.kth_threshold(scores, k)
+    diff = np.setxor1d(g, ref)
+    near = np.abs(scores[diff] - t) <= NEAR_TIE_REL * abs(t)
+    assert np.all(near), f"{what}: {int((~near).sum())} selections differ beyond the near-tie band"
+    return int(diff.shape[0]), int(near.sum())
+
+
+def check_tiles(p, res, buf, slash_tile=64):
+    """Exact checks of the GPU tile lists against the oracle's index sets."""
+    sz = buf["sizes"]
+    t = {k: v.cpu().numpy() for k, v in buf["tiles"].items()}
+    n, nq = p.n, int(sz.nq)
+    assert t["status"][0] == 0, f"device status {t['status'][0]}"
+    for (b, h), r in res["heads"].items():
+        assert int(t["kept_edges"][b, h]) == r.edges, f"kept edges of head ({b},{h}): {t['kept_edges'][b, h]} vs {r.edges}"
+        if r.kind != O.VSLASH:
+            continue
+        cover = O.slash_offset_set(r.offs, n, slash_tile)            # x + 63
+        ns = int(t["span_cnt"][b, h])
+        lo, hi = t["span_lo"][b, h, :ns], t["span_hi"][b, h, :ns]
+        got = np.zeros_like(cover)
+        for a, e in zip(lo, hi):
+            assert a <= e and a >= -63 and e < n
+            got[a + 63:e + 64] = True
+        assert np.array_equal(got, cover), f"span set of head ({b},{h})"
+        assert np.all(lo[1:] > hi[:-1] + 1), "spans not disjoint / merged"
+        clo, chi = t["chunk_lo"][b, h], t["chunk_hi"][b, h]
+        used = int(t["chunk_cnt"][b, h, nq - 1])      # chunks of the last block
+        got2 = np.zeros_like(cover)
+        for a, e in zip(clo[:used], chi[:used]):
+            assert 0 <= e - a <= 31
+            got2[a + 63:e + 64] = True
+        assert np.all(np.diff(clo[:used]) > 0), "chunks not ascending"
+        X = 64 * (nq - 1)
+        assert not np.any(got2 & ~cover), "a chunk leaves the spans"
+        assert np.array_equal(got2[:X + 64], cover[:X + 64]), "chunks miss part of the spans"
+        nch = np.array([int(np.sum(clo[:used] <= 64 * u)) for u in range(nq)])
+        assert np.array_equal(t["chunk_cnt"][b, h].astype(np.int64), nch), "chunk counts"
+        cols = np.asarray(r.cols, dtype=np.int64)
+        for u in range(nq):
+            end = min(64 * u + 63, n - 1)
+            c = cols[cols <= end]
+            exp = c[~cover[64 * u - c + 63]]
+            cc = int(t["col_cnt"][b, h, u])
+            assert np.array_equal(t["cols"][b, h, u, :cc], exp), f"columns of ({b},{h}) block {u}"
+
+
+class Timer:
+    def __init__(self, what):
+        self.what = what
+
+    def __enter__(self):
+        self.t = time.time()
+        return self
+
+    def __exit__(self, *a):
+        log(f"  [{self.what}: {time.time() - self.t:.1f}s]")

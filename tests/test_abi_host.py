@@ -1,0 +1,117 @@
+"""Host-only checks of the C interface: the library loads, exports every
+function include/minf.h declares, and argument validation answers with the
+documented status codes before anything reaches a GPU (no device pointer is
+ever dereferenced by these calls)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import long_context_prefill_amd as M
+from synth import gen
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(M.LIB_PATH):
+        from long_context_prefill_amd import build
+        build.build()
+    return M.load_library()
+
+
+def _declared():
+    txt = open(os.path.join(ROOT, "include", "minf.h")).read()
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\*?\s+(minf_\w+)\s*\(", txt, re.M)))
+
+
+def test_exports_every_declared_symbol(lib):
+    names = _declared()
+    assert set(M.EXPORTED) <= set(names)
+    for n in names:
+        assert hasattr(lib, n), n
+    assert lib.minf_version().decode().startswith("minf")
+
+
+def test_struct_layouts_match_header():
+    assert ctypes.sizeof(M.MinfProblem) == 40
+    assert ctypes.sizeof(M.MinfHeadCfg) == 32
+    assert ctypes.sizeof(M.MinfSizes) == 48
+    assert ctypes.sizeof(M.MinfTiles) == 80
+
+
+def _prob(**kw):
+    base = dict(B=1, Hq=4, Hkv=2, n=1000, dh=128, in_dtype="bf16", out_dtype="f32")
+    base.update(kw)
+    return M.make_problem(**base)
+
+
+HEADS = [gen.ashape(16, 100), gen.vslash(64, 40, 60), gen.bsparse(4), gen.vslash(32, 1000, 2000)]
+
+
+def test_query_sizes(lib):
+    s = M.minf_query_sizes(_prob(), M.make_heads(HEADS))
+    assert s.nq == 16
+    assert s.max_v == 1024          # min(1000, n) rounded up to 32
+    assert s.max_s == 1000          # min(2000, n)
+    assert s.max_kb == 4
+    assert s.max_chunks == (1000 + 63 + 31) // 32 + 1000 + 1
+    assert s.ws_bytes > 0
+
+
+@pytest.mark.parametrize("kw,heads,status", [
+    (dict(Hq=3, Hkv=2), HEADS[:3], M.MINF_EINVAL),
+    (dict(dh=96), HEADS, M.MINF_EUNSUPPORTED),
+    (dict(n=0), HEADS, M.MINF_EINVAL),
+    (dict(block=32), HEADS, M.MINF_EUNSUPPORTED),
+    (dict(slash_tile=1), HEADS, M.MINF_EUNSUPPORTED),
+    (dict(slash_tile=16), HEADS, M.MINF_EINVAL),
+    (dict(scale=-1.0), HEADS, M.MINF_EINVAL),
+    (dict(), [gen.ashape(-1, 3)] + HEADS[1:], M.MINF_EINVAL),
+    (dict(), [gen.vslash(65, 1, 1)] + HEADS[1:], M.MINF_EUNSUPPORTED),
+    (dict(), [gen.vslash(0, 1, 1)] + HEADS[1:], M.MINF_EINVAL),
+    (dict(), [gen.bsparse(0)] + HEADS[1:], M.MINF_EINVAL),
+    (dict(), [gen.bsparse(2, 8)] + HEADS[1:], M.MINF_EINVAL),
+    (dict(), [gen.HeadCfg(7)] + HEADS[1:], M.MINF_EINVAL),
+])
+def test_validation_errors(lib, kw, heads, status):
+    p = _prob(**kw)
+    with pytest.raises(M.MinfError) as e:
+        M.minf_query_sizes(p, M.make_heads(heads))
+    assert e.value.status == status
+    assert lib.minf_last_error().decode()
+
+
+def test_calls_reject_before_launch(lib):
+    """Null buffers and short workspaces are refused synchronously; the fake
+    pointers below are never dereferenced because validation fails first."""
+    p = _prob()
+    h = M.make_heads(HEADS)
+    fake = 0x1000
+    ts = M.MinfTiles()
+    st = lib.minf_vs_index(ctypes.byref(p), h, None, fake, fake, fake, None, None, fake, 1 << 40, None)
+    assert st == M.MINF_EINVAL
+    st = lib.minf_vs_index(ctypes.byref(p), h, fake, fake, fake, fake, None, None, fake, 16, None)
+    assert st == M.MINF_EWORKSPACE
+    st = lib.minf_bs_index(ctypes.byref(p), h, fake, fake, None, fake, fake, 1 << 40, None)
+    assert st == M.MINF_EINVAL
+    st = lib.minf_build_tiles(ctypes.byref(p), h, fake, fake, fake, fake, ctypes.byref(ts), fake, 1 << 40, None)
+    assert st == M.MINF_EINVAL          # tiles has no kept_edges / status
+    st = lib.minf_sparse_attn(ctypes.byref(p), h, fake, fake, None, fake, fake, ctypes.byref(ts), fake, None,
+                              fake, 1 << 40, None)
+    assert st == M.MINF_EINVAL
+    st = lib.minf_sparse_attn(ctypes.byref(p), h, fake, fake, fake, fake, fake, ctypes.byref(ts), fake, None,
+                              fake, 1 << 40, None)
+    assert st == M.MINF_EINVAL          # VS head without tile lists
+    assert "tile" in lib.minf_last_error().decode()
+
+
+def test_no_work_for_absent_kinds(lib):
+    """A layer without VS heads makes minf_vs_index a no-op that succeeds
+    (and the same for BS); nothing is queued, so no GPU is needed."""
+    p = _prob()
+    h = M.make_heads([gen.ashape(4, 8)] * 4)
+    assert lib.minf_vs_index(ctypes.byref(p), h, None, None, None, None, None, None, None, 0, None) == M.MINF_OK
+    assert lib.minf_bs_index(ctypes.byref(p), h, None, None, None, None, None, 0, None) == M.MINF_OK
