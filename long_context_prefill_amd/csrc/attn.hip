@@ -87,6 +87,15 @@ struct Ops<uint16_t, DH> {
     for (int s = 0; s < KS; ++s) a = mma_bf16(k[s], q[s], a);
     return a;
   }
+  // column mb of the 8 key rows (8x8 transpose of 16-bit values, one byte
+  // permute per output dword)
+  __device__ static __forceinline__ u32x4 vcol(const VRow (&vr)[8], int mb) {
+    const uint32_t sel = (mb & 1) ? 0x07060302u : 0x05040100u;
+    u32x4 o;
+    #pragma unroll
+    for (int q = 0; q < 4; ++q) o[q] = __builtin_amdgcn_perm(vr[2 * q + 1][mb >> 1], vr[2 * q][mb >> 1], sel);
+    return o;
+  }
 };
 
 // ---------------------------------------------------------------- fp32
@@ -139,7 +148,8 @@ __global__ __launch_bounds__(256, 1) void attn_kernel(AttnParams P) {
   constexpr int NV = O::NV;
   constexpr int KS = O::KS;
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  // wave index in a scalar register: chunk bookkeeping stays wave-uniform
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int r16 = lane & 15;
   const int g = lane >> 4;
 
@@ -160,7 +170,7 @@ __global__ __launch_bounds__(256, 1) void attn_kernel(AttnParams P) {
   if (u >= P.nq) return;
 
   const int n = P.n;
-  const int kind = P.ht.kind[h];
+  const int kind = __builtin_amdgcn_readfirstlane(P.ht.kind[h]);
   const int row0 = 64 * u;
   const size_t bh = (size_t)b * P.Hq + h;
   const T* __restrict__ Qb = reinterpret_cast<const T*>(P.Q) + bh * (size_t)n * DH;
@@ -214,6 +224,14 @@ __global__ __launch_bounds__(256, 1) void attn_kernel(AttnParams P) {
     Ca = 2 * (int)min((long long)max(P.blk_cnt[bh * P.nq + u], 0), (long long)P.max_kb);
     blkrow = P.blk_idx + (bh * P.nq + u) * P.max_kb;
   }
+  // all of these are wave-uniform; keep them in scalar registers
+  Ca = __builtin_amdgcn_readfirstlane(Ca);
+  Cb = __builtin_amdgcn_readfirstlane(Cb);
+  sink_len = __builtin_amdgcn_readfirstlane(sink_len);
+  wlo = __builtin_amdgcn_readfirstlane(wlo);
+  whi = __builtin_amdgcn_readfirstlane(whi);
+  win = __builtin_amdgcn_readfirstlane(win);
+  ncols = __builtin_amdgcn_readfirstlane(ncols);
   const int C = Ca + Cb;
 
   floatx4 acc[4][NV];
@@ -241,7 +259,7 @@ __global__ __launch_bounds__(256, 1) void attn_kernel(AttnParams P) {
       } else {
         const int kk = k - Ca;
         d.gp = colrow + 32 * kk; d.gcnt = min(32, ncols - 32 * kk);
-        d.kstart = 0; d.vlo = 0; d.vhi = -1;
+        d.kstart = 0; d.vlo = 0; d.vhi = n - 1;   // validity of listed keys is per position
       }
     } else {
       const int vb = blkrow[k >> 1];
@@ -251,6 +269,10 @@ __global__ __launch_bounds__(256, 1) void attn_kernel(AttnParams P) {
     if (d.gp) {
       d.mask = true;
     } else {
+      // a chunk owns exactly its keys [kstart, kstart+31] (its load base may be
+      // shifted to stay inside [0, n), so the range must be clipped here)
+      d.vlo = max(d.vlo, d.kstart);
+      d.vhi = min(d.vhi, d.kstart + 31);
       d.mask = (d.kstart < d.vlo) || (d.kstart + 31 > d.vhi) || (d.kstart + 31 > row0) ||
                (d.win > 0 && d.kstart < row0 + 63 - d.win + 1);
     }
@@ -263,8 +285,12 @@ __global__ __launch_bounds__(256, 1) void attn_kernel(AttnParams P) {
     for (int hh = 0; hh < 2; ++hh) {
       const int p = 16 * hh + r16;
       int key;
-      if (d.gp) key = p < d.gcnt ? d.gp[p] : 0;
-      else key = d.kstart + p;
+      if (d.gp) {
+        key = d.gp[p];                 // lists are padded to a multiple of 32 entries
+        key = p < d.gcnt ? key : 0;
+      } else {
+        key = d.kstart + p;
+      }
       O::load_k(Kb, min(max(key, 0), n - 1), g, k[hh]);
     }
     #pragma unroll
@@ -272,8 +298,8 @@ __global__ __launch_bounds__(256, 1) void attn_kernel(AttnParams P) {
       const int p = vpos(g, e);
       int key;
       if (d.gp) {
-        key = p < d.gcnt ? d.gp[p] : -1;
-        key = (key >= 0 && key < n) ? key : -1;
+        key = d.gp[p];
+        key = (p < d.gcnt && key >= 0 && key < n) ? key : -1;
       } else {
         key = d.kstart + p;
         key = (key >= d.vlo && key <= d.vhi) ? key : -1;
@@ -282,10 +308,6 @@ __global__ __launch_bounds__(256, 1) void attn_kernel(AttnParams P) {
     }
   };
 
-  auto load_vrows = [&](const int (&kv)[8], typename O::VRow (&vr)[8]) {
-    #pragma unroll
-    for (int e = 0; e < 8; ++e) O::load_v(Vb, max(kv[e], 0), r16, vr[e]);
-  };
   auto qk = [&](const typename O::KOp (&kop)[2][KS], floatx4 (&s)[2][4]) {
     #pragma unroll
     for (int nb = 0; nb < 4; ++nb) {
@@ -295,23 +317,23 @@ __global__ __launch_bounds__(256, 1) void attn_kernel(AttnParams P) {
       for (int hh = 0; hh < 2; ++hh) s[hh][nb] = O::dot(kop[hh], q, floatx4{0.f, 0.f, 0.f, 0.f});
     }
   };
-  // masks, online softmax (Eq. 7-8 with lazy rescaling) and O^T += V^T P^T
-  auto softmax_pv = [&](floatx4 (&s)[2][4], const ChunkDesc& d, const int (&kv)[8],
-                        const typename O::VRow (&vr)[8]) {
-    if (d.mask) {
+  // masks: key(e) = kb0 + ko[e] is the key of the lane's e-th S^T entry
+  // (ko[e] < 0 marks a position that is not a candidate)
+  auto apply_mask = [&](floatx4 (&s)[2][4], const ChunkDesc& d, int kb0, const int (&ko)[8]) {
+    #pragma unroll
+    for (int nb = 0; nb < 4; ++nb) {
+      const int row = row0 + 16 * nb + r16;
+      const int hi = min(d.vhi, row) - kb0;                       // key - kb0 <= hi
+      const int lo = (d.win > 0 ? max(d.vlo, row - d.win + 1) : d.vlo) - kb0;
       #pragma unroll
-      for (int nb = 0; nb < 4; ++nb) {
-        const int row = row0 + 16 * nb + r16;
-        #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const int key = kv[e];
-          bool keep = key >= 0 && key <= row;
-          if (d.win > 0) keep = keep && key >= row - d.win + 1;
-          if (!keep) s[e >> 2][nb][e & 3] = kNegInf;
-        }
+      for (int e = 0; e < 8; ++e) {
+        const int o = ko[e];
+        if (!(o >= lo && o <= hi)) s[e >> 2][nb][e & 3] = kNegInf;
       }
     }
-    // row maxima (consistent across the 4 lanes sharing a row)
+  };
+  // online softmax (Eq. 7-8 with lazy rescaling) and O^T += V^T P^T
+  auto softmax_pv = [&](floatx4 (&s)[2][4], const typename O::VRow (&vr)[8]) {
     float mx[4];
     bool need = false;
     #pragma unroll
@@ -348,16 +370,28 @@ __global__ __launch_bounds__(256, 1) void attn_kernel(AttnParams P) {
         for (int i = 0; i < 4; ++i) p[hh][nb][i] = fast_exp2(__builtin_fmaf(s[hh][nb][i], P.c, -msub));
     }
     if constexpr (sizeof(T) == 2) {
+      typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+      const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
       u32x4 pop[4];
       #pragma unroll
       for (int nb = 0; nb < 4; ++nb) {
-        pop[nb] = u32x4{pack_bf16(p[0][nb][0], p[0][nb][1]), pack_bf16(p[0][nb][2], p[0][nb][3]),
-                        pack_bf16(p[1][nb][0], p[1][nb][1]), pack_bf16(p[1][nb][2], p[1][nb][3])};
-        float ls = 0.f;
+        // packed dwords kept in scalars: bit-casting elements extracted from
+        // the u32x4 to bf16x2 was miscompiled (every extract read element 0)
+        const uint32_t w0 = pack_bf16(p[0][nb][0], p[0][nb][1]), w1 = pack_bf16(p[0][nb][2], p[0][nb][3]);
+        const uint32_t w2 = pack_bf16(p[1][nb][0], p[1][nb][1]), w3 = pack_bf16(p[1][nb][2], p[1][nb][3]);
+        pop[nb] = u32x4{w0, w1, w2, w3};
+        float ls = l_run[nb];
+        ls = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w0), ones, ls, false);
+        ls = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w1), ones, ls, false);
+        ls = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w2), ones, ls, false);
+        ls = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w3), ones, ls, false);
+        l_run[nb] = ls;
+      }
+      #pragma unroll
+      for (int mb = 0; mb < NV; ++mb) {
+        const u32x4 vop = O::vcol(vr, mb);
         #pragma unroll
-        for (int q = 0; q < 4; ++q)
-          ls += __builtin_bit_cast(float, pop[nb][q] << 16) + __builtin_bit_cast(float, pop[nb][q] & 0xffff0000u);
-        l_run[nb] += ls;
+        for (int nb = 0; nb < 4; ++nb) acc[nb][mb] = mma_bf16(vop, pop[nb], acc[nb][mb]);
       }
     } else {
       #pragma unroll
@@ -379,29 +413,76 @@ __global__ __launch_bounds__(256, 1) void attn_kernel(AttnParams P) {
     }
   };
 
-  // ---- main loop over this wave's chunks.  One register set each for K and
+  // Contiguous chunks are loaded from a wave-uniform base (the chunk's first
+  // key, clamped so that all 32 rows lie inside [0, n)) plus constant per-lane
+  // offsets; gathered chunks (vertical columns) and tiny sequences use
+  // per-lane key indices.
+  int vpos_c[8];
+  #pragma unroll
+  for (int e = 0; e < 8; ++e) vpos_c[e] = vpos(g, e);
+  const int Cfast = (n < 32) ? 0 : (kind == MINF_VSLASH ? Ca : C);
+  auto load_base = [&](const ChunkDesc& d) { return min(max(d.kstart, 0), n - 32); };
+  auto fast_load_k = [&](int lb, typename O::KOp (&kop)[2][KS]) {
+    const T* Kc = Kb + (size_t)lb * DH;
+    #pragma unroll
+    for (int hh = 0; hh < 2; ++hh) O::load_k(Kc, 16 * hh + r16, g, kop[hh]);
+  };
+  auto fast_load_v = [&](int lb, typename O::VRow (&vr)[8]) {
+    const T* Vc = Vb + (size_t)lb * DH;
+    #pragma unroll
+    for (int e = 0; e < 8; ++e) O::load_v(Vc, vpos_c[e], r16, vr[e]);
+  };
+
+  // ---- main loops over this wave's chunks.  One register set each for K and
   //      V: the next chunk's K rows are requested as soon as the current QK
   //      products have consumed the K registers, and the next V rows as soon
   //      as the PV products have consumed V, so each load has about one
   //      step of work to arrive.
-  if (wave < C) {
+  int k = wave;
+  if (k < Cfast) {
+    typename O::KOp kop[2][KS];
+    typename O::VRow vr[8];
+    ChunkDesc d, dn;
+    describe(k, d);
+    int lb = load_base(d);
+    fast_load_k(lb, kop);
+    fast_load_v(lb, vr);
+    while (true) {
+      floatx4 s[2][4];
+      qk(kop, s);
+      const int kn = k + kWaves;
+      const bool more = kn < Cfast;
+      int lbn = 0;
+      if (more) { describe(kn, dn); lbn = load_base(dn); fast_load_k(lbn, kop); }
+      if (d.mask) apply_mask(s, d, lb, vpos_c);
+      softmax_pv(s, vr);
+      k = kn;
+      if (!more) break;
+      fast_load_v(lbn, vr);
+      d = dn;
+      lb = lbn;
+    }
+  }
+  if (k < C) {
     typename O::KOp kop[2][KS];
     typename O::VRow vr[8];
     int kv[8], kvn[8];
     ChunkDesc d, dn;
-    int k = wave;
     describe(k, d);
     fetch(d, kop, kv);
-    load_vrows(kv, vr);
+    #pragma unroll
+    for (int e = 0; e < 8; ++e) O::load_v(Vb, max(kv[e], 0), r16, vr[e]);
     while (true) {
       floatx4 s[2][4];
       qk(kop, s);
       const int kn = k + kWaves;
       const bool more = kn < C;
       if (more) { describe(kn, dn); fetch(dn, kop, kvn); }
-      softmax_pv(s, d, kv, vr);
+      apply_mask(s, d, 0, kv);
+      softmax_pv(s, vr);
       if (!more) break;
-      load_vrows(kvn, vr);
+      #pragma unroll
+      for (int e = 0; e < 8; ++e) O::load_v(Vb, max(kvn[e], 0), r16, vr[e]);
       #pragma unroll
       for (int e = 0; e < 8; ++e) kv[e] = kvn[e];
       d = dn;

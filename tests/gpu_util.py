@@ -65,6 +65,12 @@ def compare_output(O_gpu, O_ref, dtype, what=""):
     mx, mean = float(d.max()) if d.size else 0.0, float(d.mean()) if d.size else 0.0
     lim = (BF16_MAX_ABS, BF16_MEAN_ABS) if dtype == "bf16" else (F32_MAX_ABS, F32_MEAN_ABS)
     log(f"  {what}: max-abs {mx:.3e} (<= {lim[0]:g}), mean-abs {mean:.3e} (<= {lim[1]:g})")
+    if d.ndim == 4 and (mx > lim[0] or mean > lim[1] or not np.all(np.isfinite(O_gpu))):
+        for b in range(d.shape[0]):
+            for h in range(d.shape[1]):
+                dr = d[b, h].max(axis=-1)
+                bad = np.nonzero(dr > lim[0])[0]
+                log(f"    head ({b},{h}): max-abs {dr.max():.3e}, {bad.size} rows over, first {bad[:12].tolist()}")
     assert np.all(np.isfinite(O_gpu)), f"{what}: non-finite output"
     assert mx <= lim[0], f"{what}: max-abs {mx} > {lim[0]}"
     assert mean <= lim[1], f"{what}: mean-abs {mean} > {lim[1]}"
