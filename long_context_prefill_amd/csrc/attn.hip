@@ -578,7 +578,7 @@ static hipError_t launch_t(const AttnParams& p, hipStream_t st) {
 }
 
 hipError_t launch_attn(const AttnParams& p, int in_bf16, int dh, hipStream_t st) {
-  if (in_bf16) return dh == 128 ? launch_t<uint16_t, 128>(p, st) : launch_t<uint16_t, 64>(p, st);
+  if (in_bf16) return dh == 128 ? launch_attn_bf16_d128(p, st) : launch_t<uint16_t, 64>(p, st);
   return dh == 128 ? launch_t<float, 128>(p, st) : launch_t<float, 64>(p, st);
 }
 

@@ -28,6 +28,8 @@ struct AttnParams {
   HeadTable ht;     // ASHAPE: a = sink, b = window
 };
 hipError_t launch_attn(const AttnParams& p, int in_bf16, int dh, hipStream_t st);
+// bf16 inputs with dh = 128 (attn_bf16.hip)
+hipError_t launch_attn_bf16_d128(const AttnParams& p, hipStream_t st);
 size_t attn_smem_bytes(int dh);
 
 // ---------------------------------------------------------------- tiles
