@@ -79,6 +79,35 @@ def attn_traffic(workload):
     return t["fetch_kib"] * 1024 * t["fetch_factor"] + t["write_kib"] * 1024 * t["write_factor"]
 
 
+def computed_pairs(p, t, buf):
+    """(query row, key) pairs the attention kernel computes: 64 x 32 per
+    chunk of every query block (sink and window chunks, slash-span chunks,
+    gathered-column chunks, two chunks per selected block).  kept / computed
+    is the tile efficiency E_h / E~_h."""
+    import numpy as np
+    from synth import gen
+    nq = (p.n + 63) // 64
+    u = np.arange(nq, dtype=np.int64)
+    total = 0
+    cc = t["chunk_cnt"].cpu().numpy() if "chunk_cnt" in t else None
+    colc = t["col_cnt"].cpu().numpy() if "col_cnt" in t else None
+    bc = buf["blk_cnt"].cpu().numpy()
+    for b in range(p.B):
+        for h, c in enumerate(p.heads):
+            if c.kind == gen.VSLASH:
+                chunks = cc[b, h].astype(np.int64) + (colc[b, h].astype(np.int64) + 31) // 32
+            elif c.kind == gen.BSPARSE:
+                chunks = 2 * bc[b, h].astype(np.int64)
+            else:
+                g, w = min(c.sink, p.n), min(c.window, p.n)
+                sink_len = np.minimum(g, np.minimum(64 * u + 64, p.n))
+                wlo = np.maximum(np.maximum(g, 64 * u - w + 1), 0)
+                whi = np.minimum(64 * u + 63, p.n - 1)
+                chunks = (sink_len + 31) // 32 + np.where((w > 0) & (whi >= wlo), (whi - wlo + 32) // 32, 0)
+            total += int(chunks.sum())
+    return total * 64 * 32
+
+
 def copy_probe(mib, reps):
     """A plain device copy of known size, for scaling the memory counters."""
     import torch
@@ -229,8 +258,8 @@ def main():
     for h, c in enumerate(p.heads):
         per_kind.setdefault(gen.KIND_NAMES[c.kind], 0)
         per_kind[gen.KIND_NAMES[c.kind]] += int(ke[:, h].sum())
-    nq = (p.n + 63) // 64
     dense = p.B * p.Hq * p.n * (p.n + 1) // 2
+    computed = computed_pairs(p, t, buf)
 
     cpu = None
     if not a.no_cpu_baseline:
@@ -265,6 +294,8 @@ def main():
         "kept_edges": kept,
         "kept_edges_by_kind": per_kind,
         "dense_causal_edges": dense,
+        "computed_pairs": computed,
+        "tile_efficiency": round(kept / computed, 4) if computed else None,
         "kept_edge_tflops": round(attn_tflops, 2),
         "frac_bf16_peak": round(attn_tflops / PEAK_BF16_TFLOPS, 4),
         "index_gbs": round(idx_gbs, 1),

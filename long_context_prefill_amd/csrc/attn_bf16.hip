@@ -64,26 +64,6 @@ __device__ __forceinline__ floatx16 mma32(u32x4 a, u32x4 b, const floatx16& c) {
                                                  0, 0, 0);
 }
 
-// 16 bytes per lane from global memory (base + voff) into LDS at dst + 16 *
-// lane; base and dst are wave-uniform.  Written as inline assembly so that
-// the compiler does not treat every later LDS read as dependent on the copy
-// (it would wait for the next chunk's copies before reading the current
-// slot); completion is waited for explicitly before the barrier of each
-// chunk.  M0 carries the LDS address and is restored afterwards; one wait
-// state separates the M0 write from the copy.
-__device__ __forceinline__ void copy16(const char* base, uint32_t voff, uint32_t dst) {
-  uint32_t keep;
-  asm volatile(
-      "s_mov_b32 %0, m0\n\t"
-      "s_mov_b32 m0, %3\n\t"
-      "s_nop 0\n\t"
-      "global_load_lds_dwordx4 %1, %2\n\t"
-      "s_mov_b32 m0, %0"
-      : "=&s"(keep)
-      : "v"(voff), "s"(base), "s"(dst)
-      : "memory");
-}
-
 __device__ __forceinline__ u32x2 read_tr(const lds_char* p) {
   const short4_t r = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4*)p);
   return __builtin_bit_cast(u32x2, r);
@@ -104,44 +84,182 @@ struct Chunk {
   int gcnt;           // entries of gp
 };
 
+// The chunk lists of one work item (batch/head bh, query block u): Ca chunks
+// of the first list (sink, slash spans or selected blocks) and Cb of the
+// second (window or gathered columns).  Shared by the cost pass of the
+// scheduler and the attention kernel.
+struct ItemLists {
+  int Ca, Cb, sink_len, wlo, whi, win, ncols;
+  const int32_t* colrow;
+  const int32_t* blkrow;
+  const int32_t* clo;
+  const int32_t* chi;
+};
+
+__device__ __forceinline__ ItemLists item_lists(const AttnParams& P, size_t bh, int h, int kind, int u) {
+  ItemLists L{0, 0, 0, 0, -1, 0, 0, nullptr, nullptr, nullptr, nullptr};
+  const int n = P.n, row0 = 64 * u;
+  if (kind == MINF_ASHAPE) {
+    const int gk = P.ht.a[h];
+    L.win = P.ht.b[h];
+    L.sink_len = min(gk, min(row0 + 64, n));
+    L.Ca = (L.sink_len + 31) >> 5;
+    if (L.win > 0) {
+      L.wlo = max(max(gk, row0 - L.win + 1), 0);
+      L.whi = min(row0 + 63, n - 1);
+      L.Cb = L.whi >= L.wlo ? ((L.whi - L.wlo + 32) >> 5) : 0;
+    }
+  } else if (kind == MINF_VSLASH) {
+    // counts are clamped to the capacities so that no list is read past its end
+    L.Ca = (int)min((long long)max(ld_uniform(P.chunk_cnt, bh * P.nq + u), 0), (long long)P.max_chunks);
+    L.ncols = (int)min((long long)max(ld_uniform(P.col_cnt, bh * P.nq + u), 0), (long long)P.max_v);
+    L.Cb = (L.ncols + 31) >> 5;
+    L.colrow = P.cols + (bh * P.nq + u) * P.max_v;
+    L.clo = P.chunk_lo + bh * P.max_chunks;
+    L.chi = P.chunk_hi + bh * P.max_chunks;
+  } else {
+    L.Ca = 2 * (int)min((long long)max(ld_uniform(P.blk_cnt, bh * P.nq + u), 0), (long long)P.max_kb);
+    L.blkrow = P.blk_idx + (bh * P.nq + u) * P.max_kb;
+  }
+  return L;
+}
+
 }  // namespace
 
-__global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2, 2)))
-void attn_bf16_d128_kernel(AttnParams P) {
+// ---------------------------------------------------------------- schedule
+// Work is spread over the 8 XCDs (blockIdx mod 8) by unit: a unit is one
+// (batch, head) pair, or a contiguous range of its query blocks when there are
+// fewer than 32 pairs.  Units are costed by their exact chunk counts and
+// assigned largest first to the least-loaded XCD (each XCD receives the same
+// number of units); an XCD walks its units in that order and each unit's query
+// blocks from the last to the first.  The 128 work-groups that run together on
+// one XCD are then consecutive blocks of one head, whose key sets are shifted
+// copies of each other, so their K/V rows are shared in that XCD's L2.
+
+__global__ __launch_bounds__(256) void attn_cost_kernel(AttnParams P, int units) {
+  const int unit = blockIdx.x;
+  long long c = 0;
+  if (unit < units) {
+    const int bhi = unit / P.sched_P, part = unit % P.sched_P;
+    const int h = bhi % P.Hq;
+    const int kind = P.ht.kind[h];
+    const int u0 = part * P.sched_R, u1 = min(u0 + P.sched_R, P.nq);
+    for (int u = u0 + (int)threadIdx.x; u < u1; u += 256) {
+      const ItemLists L = item_lists(P, (size_t)bhi, h, kind, u);
+      c += L.Ca + L.Cb + 2;   // + fixed cost of an item (Q load, output)
+    }
+  }
+  __shared__ long long sh[256];
+  sh[threadIdx.x] = c;
+  __syncthreads();
+  for (int off = 128; off > 0; off >>= 1) {
+    if ((int)threadIdx.x < off) sh[threadIdx.x] += sh[threadIdx.x + off];
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) P.sched_cost[unit] = unit < units ? sh[0] : -1;
+}
+
+__global__ __launch_bounds__(256) void attn_sched_kernel(AttnParams P, int upad) {
+  // rank by (cost descending, unit ascending)
+  for (int u = threadIdx.x; u < upad; u += 256) {
+    const long long cu = P.sched_cost[u];
+    int r = 0;
+    for (int v = 0; v < upad; ++v) {
+      const long long cv = P.sched_cost[v];
+      r += (cv > cu) || (cv == cu && v < u);
+    }
+    P.sched_order[r] = u;
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    long long load[8];
+    int cnt[8];
+    for (int x = 0; x < 8; ++x) { load[x] = 0; cnt[x] = 0; }
+    const int per = upad / 8;
+    for (int i = 0; i < upad; ++i) {
+      const int unit = P.sched_order[i];
+      const long long cu = P.sched_cost[unit];
+      int best = -1;
+      for (int x = 0; x < 8; ++x)
+        if (cnt[x] < per && (best < 0 || load[x] < load[best])) best = x;
+      P.sched[best * per + cnt[best]] = cu < 0 ? -1 : unit;
+      cnt[best]++;
+      load[best] += cu < 0 ? 0 : cu;
+    }
+  }
+}
+
+namespace {
+
+// Copies of one 32-key chunk of K (or V): four copies of 16 bytes per lane
+// from global memory (base + voff[i] + 1024 i) into LDS at dst + 1024 i + 16 *
+// lane.  The instruction offset applies to both addresses, so M0 is written
+// once.  Inline assembly keeps the compiler from treating later LDS reads as
+// dependent on the copies (it would wait for the next chunk's copies before
+// reading the current slot); completion is waited for explicitly before the
+// barrier of each chunk.  M0 is restored afterwards; one wait state separates
+// the M0 write from the first copy.
+__device__ __forceinline__ void copy_chunk(const char* base, const uint32_t (&voff)[4], uint32_t dst) {
+  uint32_t keep;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %6\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %1, %5\n\t"
+      "global_load_lds_dwordx4 %2, %5 offset:1024\n\t"
+      "global_load_lds_dwordx4 %3, %5 offset:2048\n\t"
+      "global_load_lds_dwordx4 %4, %5 offset:3072\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(keep)
+      : "v"(voff[0]), "v"(voff[1]), "v"(voff[2]), "v"(voff[3]), "s"(base), "s"(dst)
+      : "memory");
+}
+
+// The same copies with per-lane offsets that are not affine in i: one M0
+// write per copy and no instruction offset, so every voff[i] is the full,
+// non-negative byte offset of the lane's row piece from base.
+__device__ __forceinline__ void copy_rows(const char* base, const uint32_t (&voff)[4], uint32_t dst) {
+  uint32_t keep;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %6\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %1, %5\n\t"
+      "s_add_u32 m0, %6, 0x400\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %2, %5\n\t"
+      "s_add_u32 m0, %6, 0x800\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %3, %5\n\t"
+      "s_add_u32 m0, %6, 0xc00\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %4, %5\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(keep)
+      : "v"(voff[0]), "v"(voff[1]), "v"(voff[2]), "v"(voff[3]), "s"(base), "s"(dst)
+      : "memory", "scc");
+}
+
+__device__ __forceinline__ void wait_copies_and_barrier() {
+  asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+// One work item: query block u of head (b, h), both waves of the work-group.
+template <int KIND>
+__device__ __forceinline__ void attn_item(const AttnParams& P, const int b, const int h, const int u, const int slot,
+                                          lds_char* smem) {
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int l32 = lane & 31;
   const int hh = lane >> 5;
-
-  // ---- work item: each XCD (blockIdx mod 8) walks segments of 8 query
-  //      blocks x the query heads of one KV group, heaviest blocks first
-  const int bid = blockIdx.x;
-  const int xcd = bid & 7;
-  const int slot = bid >> 3;
-  const int S = 8 * P.gsz;
-  const int seg = (slot / S) * 8 + xcd;
-  const int within = slot % S;
-  if (seg >= P.n_segs) return;
-  const int kvg = seg % P.Hkv;
-  const int t2 = seg / P.Hkv;
-  const int b = t2 / P.n_utiles;
-  const int utile = P.n_utiles - 1 - (t2 % P.n_utiles);
-  const int u = utile * 8 + within / P.gsz;
-  const int h = kvg * P.gsz + within % P.gsz;
-  if (u >= P.nq) return;
-
   const int n = P.n;
-  const int kind = __builtin_amdgcn_readfirstlane(P.ht.kind[h]);
   const int row0 = 64 * u;
   const int rw0 = row0 + 32 * wave;     // this wave's first row
   const int myrow = rw0 + l32;
   const size_t bh = (size_t)b * P.Hq + h;
-  const size_t kvoff = ((size_t)b * P.Hkv + kvg) * (size_t)n * kDH;
+  const size_t kvoff = ((size_t)b * P.Hkv + h / P.gsz) * (size_t)n * kDH;
   const char* __restrict__ Kb = reinterpret_cast<const char*>(reinterpret_cast<const uint16_t*>(P.K) + kvoff);
   const char* __restrict__ Vb = reinterpret_cast<const char*>(reinterpret_cast<const uint16_t*>(P.V) + kvoff);
-
-  __shared__ __attribute__((aligned(16))) char smem_g[kSmem];
-  lds_char* smem = (lds_char*)smem_g;
 
   // ---- Q^T operand in registers: lane l holds row myrow, 16-byte pieces 2t + hh
   u32x4 q[8];
@@ -155,128 +273,111 @@ void attn_bf16_d128_kernel(AttnParams P) {
     }
   }
 
-  // ---- chunk counts of this item (wave-uniform)
-  int Ca = 0, Cb = 0, sink_len = 0, wlo = 0, whi = -1, win = 0, ncols = 0;
-  const int32_t* colrow = nullptr;
-  const int32_t* blkrow = nullptr;
-  const int32_t* clo = nullptr;
-  const int32_t* chi = nullptr;
-  if (kind == MINF_ASHAPE) {
-    const int gk = P.ht.a[h];
-    win = P.ht.b[h];
-    sink_len = min(gk, min(row0 + 64, n));
-    Ca = (sink_len + 31) >> 5;
-    if (win > 0) {
-      wlo = max(max(gk, row0 - win + 1), 0);
-      whi = min(row0 + 63, n - 1);
-      Cb = whi >= wlo ? ((whi - wlo + 32) >> 5) : 0;
-    }
-  } else if (kind == MINF_VSLASH) {
-    // counts are clamped to the capacities so that no list is read past its end
-    Ca = (int)min((long long)max(ld_uniform(P.chunk_cnt, bh * P.nq + u), 0), (long long)P.max_chunks);
-    ncols = (int)min((long long)max(ld_uniform(P.col_cnt, bh * P.nq + u), 0), (long long)P.max_v);
-    Cb = (ncols + 31) >> 5;
-    colrow = P.cols + (bh * P.nq + u) * P.max_v;
-    clo = P.chunk_lo + bh * P.max_chunks;
-    chi = P.chunk_hi + bh * P.max_chunks;
-  } else {
-    Ca = 2 * (int)min((long long)max(ld_uniform(P.blk_cnt, bh * P.nq + u), 0), (long long)P.max_kb);
-    blkrow = P.blk_idx + (bh * P.nq + u) * P.max_kb;
-  }
-  Ca = __builtin_amdgcn_readfirstlane(Ca);
-  Cb = __builtin_amdgcn_readfirstlane(Cb);
-  sink_len = __builtin_amdgcn_readfirstlane(sink_len);
-  wlo = __builtin_amdgcn_readfirstlane(wlo);
-  whi = __builtin_amdgcn_readfirstlane(whi);
-  win = __builtin_amdgcn_readfirstlane(win);
-  ncols = __builtin_amdgcn_readfirstlane(ncols);
+  // ---- chunk lists of this item (wave-uniform)
+  const ItemLists L = item_lists(P, bh, h, KIND, u);
+  const int Ca = __builtin_amdgcn_readfirstlane(L.Ca);
+  const int Cb = __builtin_amdgcn_readfirstlane(L.Cb);
   const int C = Ca + Cb;
+  if (C <= 0) {
+    // nothing kept: o = 0, lse = -inf
+    if (myrow < n) {
+      const size_t obase = (bh * n + myrow) * (size_t)kDH;
+      #pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        const int col = 32 * c + 16 * hh;
+        if (P.out_bf16) {
+          *reinterpret_cast<u32x4*>(reinterpret_cast<uint16_t*>(P.O) + obase + col / 2 * 2) = u32x4{0, 0, 0, 0};
+          *reinterpret_cast<u32x4*>(reinterpret_cast<uint16_t*>(P.O) + obase + col / 2 * 2 + 8) = u32x4{0, 0, 0, 0};
+        } else {
+          #pragma unroll
+          for (int q4 = 0; q4 < 4; ++q4)
+            *reinterpret_cast<floatx4*>(reinterpret_cast<float*>(P.O) + obase + col + 4 * q4) = floatx4{0.f, 0.f, 0.f, 0.f};
+        }
+      }
+      if (hh == 0 && P.lse) P.lse[bh * n + myrow] = kNegInf;
+    }
+    return;
+  }
+  const int sink_len = __builtin_amdgcn_readfirstlane(L.sink_len);
+  const int wlo = __builtin_amdgcn_readfirstlane(L.wlo);
+  const int whi = __builtin_amdgcn_readfirstlane(L.whi);
+  const int win = __builtin_amdgcn_readfirstlane(L.win);
+  const int ncols = __builtin_amdgcn_readfirstlane(L.ncols);
 
   auto describe = [&](int k, Chunk& d) {
     d.gp = nullptr; d.gcnt = 0; d.win = 0;
-    if (kind == MINF_ASHAPE) {
+    if constexpr (KIND == MINF_ASHAPE) {
       if (k < Ca) {
-        d.kstart = 32 * k; d.vlo = 0; d.vhi = sink_len - 1;
+        d.kstart = 32 * k; d.vlo = d.kstart; d.vhi = min(d.kstart + 31, sink_len - 1);
       } else {
-        d.kstart = wlo + 32 * (k - Ca); d.vlo = wlo; d.vhi = whi; d.win = win;
+        d.kstart = wlo + 32 * (k - Ca); d.vlo = d.kstart; d.vhi = min(d.kstart + 31, whi); d.win = win;
       }
-    } else if (kind == MINF_VSLASH) {
+    } else if constexpr (KIND == MINF_VSLASH) {
       if (k < Ca) {
-        const int lo = ld_uniform(clo, k), hi = ld_uniform(chi, k);
+        const int lo = ld_uniform(L.clo, k), hi = ld_uniform(L.chi, k);
         d.kstart = row0 - hi; d.vlo = max(0, d.kstart); d.vhi = min(row0 - lo, n - 1);
       } else {
         const int kk = k - Ca;
-        d.gp = colrow + 32 * kk; d.gcnt = min(32, ncols - 32 * kk);
+        d.gp = L.colrow + 32 * kk; d.gcnt = min(32, ncols - 32 * kk);
         d.kstart = 0; d.vlo = 0; d.vhi = n - 1;
       }
     } else {
-      const int vb = ld_uniform(blkrow, k >> 1);
+      const int vb = ld_uniform(L.blkrow, k >> 1);
       d.kstart = 64 * vb + 32 * (k & 1); d.vlo = d.kstart; d.vhi = min(d.kstart + 31, n - 1);
       if (vb < 0 || vb > u) { d.kstart = 0; d.vlo = 1; d.vhi = 0; }   // not a causal block: keep nothing
-    }
-    if (!d.gp) {
-      // a chunk owns exactly its keys [kstart, kstart + 31]
-      d.vlo = max(d.vlo, d.kstart);
-      d.vhi = min(d.vhi, d.kstart + 31);
     }
   };
 
   // ---- copy offsets.  Wave w copies rows 16w + 4i + lane/16 (i = 0..3) of
   //      each tile; lane l writes LDS piece l%16 of its row, which holds the
-  //      row's piece (l%16) ^ swz(row).
+  //      row's piece (l%16) ^ swz(row).  The 1024 i of each copy is the
+  //      instruction offset.
   const int crow0 = 16 * wave + (lane >> 4);
   const int cpiece = lane & 15;
   uint32_t koff[4], voff[4];
   #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int r = crow0 + 4 * i;
-    koff[i] = (uint32_t)(r * kRowB + 16 * (cpiece ^ (r & 15)));
-    voff[i] = (uint32_t)(r * kRowB + 16 * (cpiece ^ (4 * (r & 3))));
+    koff[i] = (uint32_t)(r * kRowB + 16 * (cpiece ^ (r & 15)) - 1024 * i);
+    voff[i] = (uint32_t)(r * kRowB + 16 * (cpiece ^ (4 * (r & 3))) - 1024 * i);
   }
-  const uint32_t lds_base = (uint32_t)(uintptr_t)smem;
-  auto issue = [&](const Chunk& d, int sl) {
-    const uint32_t lk = __builtin_amdgcn_readfirstlane(lds_base + sl * kSlotB + 4096 * wave);
-    const uint32_t lv = lk + kTileB;
+  const uint32_t lds_base = (uint32_t)(uintptr_t)smem + 4096 * wave;
+  // K rows (V rows) of chunk d into the K (V) half of slot sl
+  auto issue = [&](const Chunk& d, int sl, bool is_v) {
+    const char* src = is_v ? Vb : Kb;
+    const uint32_t dst = __builtin_amdgcn_readfirstlane(lds_base + sl * kSlotB + (is_v ? kTileB : 0));
     if (!d.gp && d.kstart >= 0 && d.kstart + 31 < n) {
-      const char* kb = Kb + (size_t)d.kstart * kRowB;
-      const char* vb = Vb + (size_t)d.kstart * kRowB;
-      #pragma unroll
-      for (int i = 0; i < 4; ++i) copy16(kb, koff[i], lk + 1024 * i);
-      #pragma unroll
-      for (int i = 0; i < 4; ++i) copy16(vb, voff[i], lv + 1024 * i);
+      copy_chunk(src + (size_t)d.kstart * kRowB, is_v ? voff : koff, dst);
     } else {
       // per-lane rows: clamped into [0, n) (the excess keys are masked) or
       // gathered from the column list; all keys are read before any copy
-      uint32_t rb[4];
+      uint32_t o[4];
       #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int r = crow0 + 4 * i;
         int key = d.kstart + r;
         if (d.gp) key = r < d.gcnt ? d.gp[r] : 0;
-        rb[i] = (uint32_t)min(max(key, 0), n - 1) * kRowB;
+        const uint32_t rb = (uint32_t)min(max(key, 0), n - 1) * kRowB;
+        o[i] = rb + 16 * (cpiece ^ (is_v ? 4 * (r & 3) : (r & 15)));
       }
-      #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int r = crow0 + 4 * i;
-        copy16(Kb, rb[i] + 16 * (cpiece ^ (r & 15)), lk + 1024 * i);
-        copy16(Vb, rb[i] + 16 * (cpiece ^ (4 * (r & 3))), lv + 1024 * i);
-      }
+      copy_rows(src, o, dst);
     }
   };
 
-  // ---- operand read offsets
+  // ---- operand read offsets within a slot
   // K: lane l reads row l%32, piece 2t + hh
-  uint32_t kr[8];
-  #pragma unroll
-  for (int t = 0; t < 8; ++t) kr[t] = (uint32_t)(l32 * kRowB + 16 * ((2 * t + hh) ^ (l32 & 15)));
   // V^T (transposing read): lane 16G + 4r + qq supplies row 16s + 8rho + 4(G/2) + r,
-  // columns 32mb + 16(G%2) + 4qq .. +3
-  uint32_t vr[4];
+  // columns 32mb + 16(G%2) + 4qq .. +3 (the 16s + 8rho rows are instruction offsets)
+  const uint32_t sbase = (uint32_t)(uintptr_t)smem;
+  uint32_t kofs[8], vofs[4];
   {
     const int G = lane >> 4, r = (lane >> 2) & 3, qq = lane & 3;
     #pragma unroll
+    for (int t = 0; t < 8; ++t) kofs[t] = (uint32_t)(l32 * kRowB + 16 * ((2 * t + hh) ^ (l32 & 15)));
+    #pragma unroll
     for (int mb = 0; mb < 4; ++mb)
-      vr[mb] = (uint32_t)((4 * (G >> 1) + r) * kRowB + 16 * (4 * (mb ^ r) + 2 * (G & 1) + (qq >> 1)) + 8 * (qq & 1));
+      vofs[mb] = (uint32_t)(kTileB + (4 * (G >> 1) + r) * kRowB + 16 * (4 * (mb ^ r) + 2 * (G & 1) + (qq >> 1)) +
+                            8 * (qq & 1));
   }
 
   floatx16 acc[4];
@@ -293,8 +394,8 @@ void attn_bf16_d128_kernel(AttnParams P) {
   // What a chunk needs from this wave (wave-uniform): whether any of its keys
   // survives for the wave's rows, and whether some pair needs the per-element
   // test.  For a gathered chunk that needs the test, gbits gets bit i set when
-  // the lane's i-th key (position 8(i/4) + 4hh + i%4) is kept for its row;
-  // those keys are loaded here, before the next chunk's copies are in flight.
+  // the lane's i-th key (position 8(i/4) + 4hh + i%4) is kept for its row.
+  // Called while no copy is in flight (its vector loads are waited for).
   struct Plan { bool any, mask; uint32_t gbits; };
   auto plan = [&](const Chunk& d) {
     Plan pl{false, false, 0u};
@@ -322,21 +423,13 @@ void attn_bf16_d128_kernel(AttnParams P) {
     }
     return pl;
   };
-
-  auto compute = [&](const Chunk& d, const Plan& pl, int sl) {
-    if (!pl.any) return;
-    const bool mask = pl.mask;
-    const lds_char* ks = smem + sl * kSlotB;
-    const lds_char* vs = ks + kTileB;
-
-    floatx16 s;
-    #pragma unroll
-    for (int i = 0; i < 16; ++i) s[i] = 0.f;
-    #pragma unroll
-    for (int t = 0; t < 8; ++t) s = mma32(*(lds_u32x4*)(ks + kr[t]), q[t], s);
-
-    if (mask) {
-      // element i holds key position 8(i/4) + 4hh + i%4 of the chunk
+  // exclusion (section 5.1): pairs outside the candidate set are -inf before
+  // the maximum; element i holds key position 8(i/4) + 4hh + i%4 of the chunk
+  auto apply_mask = [&](floatx16& s, const Chunk& d, const Plan& pl) {
+    if (!pl.any) {
+      #pragma unroll
+      for (int i = 0; i < 16; ++i) s[i] = kNegInf;
+    } else if (pl.mask) {
       if (d.gp) {
         #pragma unroll
         for (int i = 0; i < 16; ++i)
@@ -351,10 +444,94 @@ void attn_bf16_d128_kernel(AttnParams P) {
         }
       }
     }
+  };
+  auto read_k = [&](int sl, u32x4 (&kop)[8]) {
+    #pragma unroll
+    for (int t = 0; t < 8; ++t) kop[t] = *(lds_u32x4*)(uintptr_t)(sbase + sl * kSlotB + kofs[t]);
+  };
+  auto read_v = [&](int sl, u32x4 (&vop)[2][4]) {
+    #pragma unroll
+    for (int st = 0; st < 2; ++st) {
+      #pragma unroll
+      for (int mb = 0; mb < 4; ++mb) {
+        const lds_char* pv = (const lds_char*)(uintptr_t)(sbase + sl * kSlotB + vofs[mb]) + 4096 * st;
+        const u32x2 lo = read_tr(pv);
+        const u32x2 hi2 = read_tr(pv + 2048);
+        vop[st][mb] = u32x4{lo[0], lo[1], hi2[0], hi2[1]};
+      }
+    }
+  };
+  auto qk = [&](const u32x4 (&kop)[8]) {
+    floatx16 s;
+    #pragma unroll
+    for (int i = 0; i < 16; ++i) s[i] = 0.f;
+    #pragma unroll
+    for (int t = 0; t < 8; ++t) s = mma32(kop[t], q[t], s);
+    return s;
+  };
 
-    // online softmax, lazy rescaling
-    float mx = fmaxf(fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3])), fmaxf(fmaxf(s[4], s[5]), fmaxf(s[6], s[7])));
-    mx = fmaxf(mx, fmaxf(fmaxf(fmaxf(s[8], s[9]), fmaxf(s[10], s[11])), fmaxf(fmaxf(s[12], s[13]), fmaxf(s[14], s[15]))));
+  // Walk order.  The 128 work-groups that run together on one XCD are
+  // consecutive query blocks of one head and start together, so the order is
+  // chosen to make them read the same keys at the same step (Eq. 7-8 do not
+  // depend on the order):
+  // * Vertical-Slash: chunks from last to first, i.e. gathered columns (the
+  //   same for every block), then slash spans by ascending key; block u's
+  //   spans are block (u-1)'s shifted by 64 keys plus the chunks of offsets in
+  //   (64(u-1), 64u], so neighbouring blocks stay close in key;
+  // * A-shape: block u's window is block (u+1)'s shifted down by two chunks,
+  //   so the walk starts two chunks further along per dispatch position;
+  // * Block-Sparse: selected blocks in ascending order.
+  const int step = KIND == MINF_VSLASH ? -1 : 1;
+  int kc = KIND == MINF_VSLASH ? C - 1 : (KIND == MINF_ASHAPE ? (2 * (slot & 127)) % C : 0);
+  auto advance = [&]() {
+    kc += step;
+    kc = kc == C ? 0 : (kc < 0 ? C - 1 : kc);
+  };
+
+  // ---- software pipeline.  Chunk j lives in slot j%2 (K and V halves).  In
+  //      iteration j the wave computes the softmax and P.V of chunk j and,
+  //      interleaved with that softmax, the Q.K products of chunk j+1; the
+  //      copies issued in iteration j are V of chunk j+1 and K of chunk j+2, so
+  //      every slot half is rewritten only after both waves have passed the
+  //      barrier that ends its last use.
+  Chunk d0, d1, d2;
+  describe(kc, d0);
+  issue(d0, 0, false);
+  issue(d0, 0, true);
+  if (C > 1) {
+    advance();
+    describe(kc, d1);
+    issue(d1, 1, false);
+  }
+  wait_copies_and_barrier();
+  Plan p0 = plan(d0);
+  floatx16 s_cur;
+  {
+    u32x4 kop[8];
+    read_k(0, kop);
+    s_cur = qk(kop);
+  }
+
+  auto iteration = [&](const int j, const int sl) {
+    // slot sl holds K and V of chunk j, slot sl^1 holds K of chunk j+1
+    u32x4 kop[8], vop[2][4];
+    const bool more = j + 1 < C;
+    read_k(sl ^ 1, kop);
+    Plan p1{false, false, 0u};
+    if (more) p1 = plan(d1);
+    if (more) issue(d1, sl ^ 1, true);
+    if (j + 2 < C) {
+      advance();
+      describe(kc, d2);
+      issue(d2, sl, false);
+    }
+    apply_mask(s_cur, d0, p0);
+
+    // online softmax of chunk j with lazy rescaling
+    float mx = fmaxf(fmaxf(fmaxf(s_cur[0], s_cur[1]), fmaxf(s_cur[2], s_cur[3])),
+                     fmaxf(fmaxf(s_cur[4], s_cur[5]), fmaxf(s_cur[6], s_cur[7])));
+    mx = fmaxf(mx, fmaxf(fmaxf(fmaxf(s_cur[8], s_cur[9]), fmaxf(s_cur[10], s_cur[11])),
+                         fmaxf(fmaxf(s_cur[12], s_cur[13]), fmaxf(s_cur[14], s_cur[15]))));
     mx *= cfac;
     if (__builtin_amdgcn_ballot_w64(mx > m_run + kTau)) {
       const float pm = fmaxf(mx, __shfl_xor(mx, 32));      // the row's other 16 keys
@@ -365,51 +542,49 @@ void attn_bf16_d128_kernel(AttnParams P) {
       l_run *= alpha;
       m_run = mn;
     }
+    // Q.K of chunk j+1 (8 products) interleaved with the exponentials,
+    // conversions and row sums of chunk j (48 vector instructions)
+    const floatx16 s_next = qk(kop);
+    read_v(sl, vop);
     u32x4 pb[2];
     #pragma unroll
     for (int st = 0; st < 2; ++st) {
       uint32_t w[4];
       #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const float p0 = fast_exp2(__builtin_fmaf(s[8 * st + 2 * e], cfac, -m_run));
-        const float p1 = fast_exp2(__builtin_fmaf(s[8 * st + 2 * e + 1], cfac, -m_run));
-        w[e] = pack_bf16(p0, p1);
+        const float p0f = fast_exp2(__builtin_fmaf(s_cur[8 * st + 2 * e], cfac, -m_run));
+        const float p1f = fast_exp2(__builtin_fmaf(s_cur[8 * st + 2 * e + 1], cfac, -m_run));
+        w[e] = pack_bf16(p0f, p1f);
         l_run = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w[e]), ones, l_run, false);
       }
       pb[st] = u32x4{w[0], w[1], w[2], w[3]};
     }
-
-    // O^T += V^T P^T
+    // (the transposing V reads of chunk j go in after half of the products,
+    // when half of the K operand registers are free)
     #pragma unroll
-    for (int st = 0; st < 2; ++st) {
-      #pragma unroll
-      for (int mb = 0; mb < 4; ++mb) {
-        const lds_char* p = vs + vr[mb] + 4096 * st;
-        const u32x2 lo = read_tr(p);
-        const u32x2 hi2 = read_tr(p + 2048);
-        const u32x4 va = {lo[0], lo[1], hi2[0], hi2[1]};
-        acc[mb] = mma32(va, pb[st], acc[mb]);
-      }
+    for (int g = 0; g < 8; ++g) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one matrix product
+      __builtin_amdgcn_sched_group_barrier(0x402, 6, 0);   // six vector instructions
+      if (g == 3 || g == 7) __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);   // eight LDS reads
     }
+    // O^T += V^T P^T for chunk j
+    #pragma unroll
+    for (int st = 0; st < 2; ++st)
+      #pragma unroll
+      for (int mb = 0; mb < 4; ++mb) acc[mb] = mma32(vop[st][mb], pb[st], acc[mb]);
+    s_cur = s_next;
+    d0 = d1;
+    d1 = d2;
+    p0 = p1;
   };
 
-  // ---- main loop: copy chunk j+1 while chunk j is computed
-  if (C > 0) {
-    Chunk dc, dn;
-    describe(0, dc);
-    issue(dc, 0);
-    for (int j = 0; j < C; ++j) {
-      // this wave's copies of chunk j have landed; after the barrier the other
-      // wave's have too, and both have finished reading chunk j-1's slot
-      asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
-      const Plan pl = plan(dc);
-      if (j + 1 < C) {
-        describe(j + 1, dn);
-        issue(dn, (j + 1) & 1);
-      }
-      compute(dc, pl, j & 1);
-      dc = dn;
-    }
+  for (int j = 0; j < C; j += 2) {
+    iteration(j, 0);
+    if (j + 1 >= C) break;
+    wait_copies_and_barrier();
+    iteration(j + 1, 1);
+    if (j + 2 >= C) break;
+    wait_copies_and_barrier();
   }
 
   // ---- finish: the row's sum over both lane halves, O = acc / l, LSE
@@ -436,10 +611,37 @@ void attn_bf16_d128_kernel(AttnParams P) {
   }
 }
 
+}  // namespace
+
+__global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void attn_bf16_d128_kernel(AttnParams P) {
+  // ---- work item from the per-XCD schedule
+  const int xcd = blockIdx.x & 7;
+  const int slot = blockIdx.x >> 3;
+  const int k_unit = slot / P.sched_R;
+  if (k_unit >= P.sched_per_xcd) return;
+  const int unit = ld_uniform(P.sched, (int64_t)xcd * P.sched_per_xcd + k_unit);
+  if (unit < 0) return;
+  const int bhi = unit / P.sched_P;
+  const int u = (unit % P.sched_P) * P.sched_R + (P.sched_R - 1 - slot % P.sched_R);
+  if (u >= P.nq) return;
+  const int b = bhi / P.Hq;
+  const int h = bhi % P.Hq;
+
+  __shared__ __attribute__((aligned(16))) char smem_g[kSmem];
+  lds_char* smem = (lds_char*)smem_g;
+  const int kind = __builtin_amdgcn_readfirstlane(P.ht.kind[h]);
+  if (kind == MINF_VSLASH) attn_item<MINF_VSLASH>(P, b, h, u, slot, smem);
+  else if (kind == MINF_BSPARSE) attn_item<MINF_BSPARSE>(P, b, h, u, slot, smem);
+  else attn_item<MINF_ASHAPE>(P, b, h, u, slot, smem);
+}
+
 hipError_t launch_attn_bf16_d128(const AttnParams& p, hipStream_t st) {
-  const int S = 8 * p.gsz;
-  const int rounds = (p.n_segs + 7) / 8;
-  const unsigned grid = (unsigned)rounds * 8u * (unsigned)S;
+  const int units = p.B * p.Hq * p.sched_P;
+  const int upad = 8 * p.sched_per_xcd;
+  hipLaunchKernelGGL(attn_cost_kernel, dim3(upad), dim3(256), 0, st, p, units);
+  hipLaunchKernelGGL(attn_sched_kernel, dim3(1), dim3(256), 0, st, p, upad);
+  const unsigned grid = (unsigned)upad * (unsigned)p.sched_R;
   hipLaunchKernelGGL(attn_bf16_d128_kernel, dim3(grid), dim3(128), 0, st, p);
   return hipGetLastError();
 }

@@ -140,8 +140,21 @@ minf::VsWs vs_ws(const minf_problem* p, const Derived& d) {
   return minf::vs_workspace(p->B, p->Hq, p->n, (int)d.nq);
 }
 
+struct AttnWs { size_t cost, order, sched, total; int P, R, per_xcd; };
+AttnWs attn_ws(const minf_problem* p, const Derived& d) {
+  Carve c;
+  AttnWs w;
+  minf::attn_sched_shape(p->B, p->Hq, d.nq, &w.P, &w.R, &w.per_xcd);
+  const size_t upad = 8 * (size_t)w.per_xcd;
+  w.cost = c.take(upad * 8);
+  w.order = c.take(upad * 4);
+  w.sched = c.take(upad * 4);
+  w.total = c.off;
+  return w;
+}
+
 size_t ws_total(const minf_problem* p, const Derived& d) {
-  size_t t = tiles_ws(p, d).total;
+  size_t t = std::max(tiles_ws(p, d).total, attn_ws(p, d).total);
   if (d.has_bs) t = std::max(t, bs_ws(p, d).total);
   if (d.has_vs) t = std::max(t, vs_ws(p, d).total);
   return std::max<size_t>(t, 256);
@@ -272,12 +285,17 @@ minf_status minf_sparse_attn(const minf_problem* prob, const minf_head_cfg* head
   Derived d;
   minf_status s = validate(prob, heads, &d);
   if (s != MINF_OK) return s;
-  (void)ws; (void)ws_bytes;
   if (!Q || !K || !V || !O) return fail(MINF_EINVAL, "null Q, K, V or O");
   if (d.has_bs && (!blk_idx || !blk_cnt)) return fail(MINF_EINVAL, "a Block-Sparse head needs blk_idx and blk_cnt");
   if (d.has_vs && (!tiles || !tiles->chunk_lo || !tiles->chunk_hi || !tiles->chunk_cnt || !tiles->cols || !tiles->col_cnt))
     return fail(MINF_EINVAL, "a Vertical-Slash head needs the tile lists from minf_build_tiles");
+  if ((s = check_ws(prob, d, ws, ws_bytes)) != MINF_OK) return s;
+  const AttnWs w = attn_ws(prob, d);
   minf::AttnParams a{};
+  a.sched_cost = reinterpret_cast<int64_t*>(static_cast<char*>(ws) + w.cost);
+  a.sched_order = reinterpret_cast<int32_t*>(static_cast<char*>(ws) + w.order);
+  a.sched = reinterpret_cast<int32_t*>(static_cast<char*>(ws) + w.sched);
+  a.sched_P = w.P; a.sched_R = w.R; a.sched_per_xcd = w.per_xcd;
   a.Q = Q; a.K = K; a.V = V; a.O = O; a.lse = lse;
   a.blk_idx = blk_idx; a.blk_cnt = blk_cnt;
   if (d.has_vs) {
