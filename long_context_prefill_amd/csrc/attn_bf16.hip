@@ -127,27 +127,70 @@ __device__ __forceinline__ ItemLists item_lists(const AttnParams& P, size_t bh, 
 }  // namespace
 
 // ---------------------------------------------------------------- schedule
-// Work is spread over the 8 XCDs (blockIdx mod 8) by unit: a unit is one
-// (batch, head) pair, or a contiguous range of its query blocks when there are
-// fewer than 32 pairs.  Units are costed by their exact chunk counts and
-// assigned largest first to the least-loaded XCD (each XCD receives the same
-// number of units); an XCD walks its units in that order and each unit's query
-// blocks from the last to the first.  The 128 work-groups that run together on
-// one XCD are then consecutive blocks of one head, whose key sets are shifted
-// copies of each other, so their K/V rows are shared in that XCD's L2.
+// Work items are (batch, head, query block) triples, handed out through one
+// queue per XCD: the attention kernel runs persistent work-groups (four per
+// CU) and work-group i serves the queue of XCD i mod 8, the XCD the
+// hardware dispatches it to.  Items are grouped into units:
+// * a Vertical-Slash or A-shape unit is one (batch, head) pair, or a
+//   contiguous range of its query blocks when there are fewer than 32 pairs;
+//   its blocks are queued from the last to the first;
+// * a Block-Sparse unit holds every Block-Sparse head of one (batch, KV
+//   group) over such a block range, interleaved per query block: heads that
+//   share K and V and select nearly the same key blocks run side by side.
+// Units are costed by their exact chunk counts and assigned largest first to
+// the least-loaded XCD.  The work-groups that run together on one XCD are
+// then consecutive query blocks of one head (or one KV group), whose key sets
+// largely coincide, so their K/V rows are shared in that XCD's L2.
 
-__global__ __launch_bounds__(256) void attn_cost_kernel(AttnParams P, int units) {
+// Block-Sparse heads of h's KV group: their number, and h's rank among them.
+__device__ __forceinline__ int bs_group(const AttnParams& P, int h, int* rank) {
+  const int g0 = (h / P.gsz) * P.gsz;
+  int cnt = 0, r = -1;
+  for (int k = g0; k < g0 + P.gsz; ++k) {
+    if (P.ht.kind[k] != MINF_BSPARSE) continue;
+    if (k == h) r = cnt;
+    ++cnt;
+  }
+  *rank = r;
+  return cnt;
+}
+// k-th Block-Sparse head of the KV group that starts at head g0
+__device__ __forceinline__ int bs_head(const AttnParams& P, int g0, int k) {
+  for (int j = g0; j < g0 + P.gsz; ++j)
+    if (P.ht.kind[j] == MINF_BSPARSE && k-- == 0) return j;
+  return g0;
+}
+// Items of a unit (0 for the units of Block-Sparse heads other than the
+// first of their group, whose items the first head's unit carries).
+__device__ __forceinline__ int unit_items(const AttnParams& P, int unit, int* u0, int* u1, int* nbs) {
+  const int bhi = unit / P.sched_P, part = unit % P.sched_P;
+  const int h = bhi % P.Hq;
+  *u0 = part * P.sched_R;
+  *u1 = min(*u0 + P.sched_R, P.nq);
+  *nbs = 1;
+  if (*u0 >= *u1) return 0;
+  if (P.ht.kind[h] == MINF_BSPARSE) {
+    int r;
+    *nbs = bs_group(P, h, &r);
+    if (r != 0) return 0;
+    return (*u1 - *u0) * *nbs;
+  }
+  return *u1 - *u0;
+}
+
+__global__ __launch_bounds__(256) void attn_cost_kernel(AttnParams P) {
   const int unit = blockIdx.x;
+  int u0, u1, nbs;
+  const int items = unit_items(P, unit, &u0, &u1, &nbs);
+  const int bhi = unit / P.sched_P;
+  const int b = bhi / P.Hq, h = bhi % P.Hq;
+  const int kind = P.ht.kind[h];
   long long c = 0;
-  if (unit < units) {
-    const int bhi = unit / P.sched_P, part = unit % P.sched_P;
-    const int h = bhi % P.Hq;
-    const int kind = P.ht.kind[h];
-    const int u0 = part * P.sched_R, u1 = min(u0 + P.sched_R, P.nq);
-    for (int u = u0 + (int)threadIdx.x; u < u1; u += 256) {
-      const ItemLists L = item_lists(P, (size_t)bhi, h, kind, u);
-      c += L.Ca + L.Cb + 2;   // + fixed cost of an item (Q load, output)
-    }
+  for (int i = (int)threadIdx.x; i < items; i += 256) {
+    const int u = u1 - 1 - i / nbs;
+    const int hh = kind == MINF_BSPARSE ? bs_head(P, (h / P.gsz) * P.gsz, i % nbs) : h;
+    const ItemLists L = item_lists(P, (size_t)b * P.Hq + hh, hh, kind, u);
+    c += L.Ca + L.Cb + 2;   // + fixed cost of an item (Q load, output)
   }
   __shared__ long long sh[256];
   sh[threadIdx.x] = c;
@@ -156,15 +199,16 @@ __global__ __launch_bounds__(256) void attn_cost_kernel(AttnParams P, int units)
     if ((int)threadIdx.x < off) sh[threadIdx.x] += sh[threadIdx.x + off];
     __syncthreads();
   }
-  if (threadIdx.x == 0) P.sched_cost[unit] = unit < units ? sh[0] : -1;
+  if (threadIdx.x == 0) P.sched_cost[unit] = items > 0 ? sh[0] : -1;
 }
 
-__global__ __launch_bounds__(256) void attn_sched_kernel(AttnParams P, int upad) {
+__global__ __launch_bounds__(256) void attn_sched_kernel(AttnParams P) {
+  const int U = P.sched_units;
   // rank by (cost descending, unit ascending)
-  for (int u = threadIdx.x; u < upad; u += 256) {
+  for (int u = threadIdx.x; u < U; u += 256) {
     const long long cu = P.sched_cost[u];
     int r = 0;
-    for (int v = 0; v < upad; ++v) {
+    for (int v = 0; v < U; ++v) {
       const long long cv = P.sched_cost[v];
       r += (cv > cu) || (cv == cu && v < u);
     }
@@ -175,17 +219,43 @@ __global__ __launch_bounds__(256) void attn_sched_kernel(AttnParams P, int upad)
     long long load[8];
     int cnt[8];
     for (int x = 0; x < 8; ++x) { load[x] = 0; cnt[x] = 0; }
-    const int per = upad / 8;
-    for (int i = 0; i < upad; ++i) {
+    for (int i = 0; i < U; ++i) {
       const int unit = P.sched_order[i];
       const long long cu = P.sched_cost[unit];
-      int best = -1;
-      for (int x = 0; x < 8; ++x)
-        if (cnt[x] < per && (best < 0 || load[x] < load[best])) best = x;
-      P.sched[best * per + cnt[best]] = cu < 0 ? -1 : unit;
-      cnt[best]++;
-      load[best] += cu < 0 ? 0 : cu;
+      if (cu < 0) { P.unit_xcd[unit] = -1; continue; }
+      int best = 0;
+      for (int x = 1; x < 8; ++x)
+        if (load[x] < load[best]) best = x;
+      int u0, u1, nbs;
+      P.unit_xcd[unit] = best;
+      P.unit_off[unit] = cnt[best];
+      cnt[best] += unit_items(P, unit, &u0, &u1, &nbs);
+      load[best] += cu;
     }
+    int off = 0;
+    for (int x = 0; x < 8; ++x) {
+      P.queue_meta[x] = off;
+      P.queue_meta[8 + x] = cnt[x];
+      P.queue_meta[16 + x] = 0;     // the queue counters start at zero
+      off += cnt[x];
+    }
+  }
+}
+
+__global__ __launch_bounds__(256) void attn_fill_kernel(AttnParams P) {
+  const int unit = blockIdx.x;
+  const int x = P.unit_xcd[unit];
+  if (x < 0) return;
+  int u0, u1, nbs;
+  const int items = unit_items(P, unit, &u0, &u1, &nbs);
+  const int bhi = unit / P.sched_P;
+  const int b = bhi / P.Hq, h = bhi % P.Hq;
+  const bool bs = P.ht.kind[h] == MINF_BSPARSE;
+  int32_t* q = P.queue + P.queue_meta[x] + P.unit_off[unit];
+  for (int i = (int)threadIdx.x; i < items; i += 256) {
+    const int u = u1 - 1 - i / nbs;
+    const int hh = bs ? bs_head(P, (h / P.gsz) * P.gsz, i % nbs) : h;
+    q[i] = ((b * P.Hq + hh) * P.nq) + u;
   }
 }
 
@@ -240,8 +310,11 @@ __device__ __forceinline__ void copy_rows(const char* base, const uint32_t (&vof
       : "memory", "scc");
 }
 
+// This wave's copies have landed and its LDS reads have returned; after the
+// barrier the same holds for the other wave, so both may read what was copied
+// and rewrite what was read.
 __device__ __forceinline__ void wait_copies_and_barrier() {
-  asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
+  asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
 // One work item: query block u of head (b, h), both waves of the work-group.
@@ -446,8 +519,9 @@ __device__ __forceinline__ void attn_item(const AttnParams& P, const int b, cons
     }
   };
   auto read_k = [&](int sl, u32x4 (&kop)[8]) {
+    const uint32_t base = sbase + sl * kSlotB;
     #pragma unroll
-    for (int t = 0; t < 8; ++t) kop[t] = *(lds_u32x4*)(uintptr_t)(sbase + sl * kSlotB + kofs[t]);
+    for (int t = 0; t < 8; ++t) kop[t] = *(lds_u32x4*)(uintptr_t)(base + kofs[t]);
   };
   auto read_v = [&](int sl, u32x4 (&vop)[2][4]) {
     #pragma unroll
@@ -511,6 +585,8 @@ __device__ __forceinline__ void attn_item(const AttnParams& P, const int b, cons
     read_k(0, kop);
     s_cur = qk(kop);
   }
+  // iteration 0 rewrites the K half of slot 0, which both waves just read
+  wait_copies_and_barrier();
 
   auto iteration = [&](const int j, const int sl) {
     // slot sl holds K and V of chunk j, slot sl^1 holds K of chunk j+1
@@ -615,34 +691,47 @@ __device__ __forceinline__ void attn_item(const AttnParams& P, const int b, cons
 
 __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void attn_bf16_d128_kernel(AttnParams P) {
-  // ---- work item from the per-XCD schedule
+  // persistent: take items from this XCD's queue until it is empty
   const int xcd = blockIdx.x & 7;
-  const int slot = blockIdx.x >> 3;
-  const int k_unit = slot / P.sched_R;
-  if (k_unit >= P.sched_per_xcd) return;
-  const int unit = ld_uniform(P.sched, (int64_t)xcd * P.sched_per_xcd + k_unit);
-  if (unit < 0) return;
-  const int bhi = unit / P.sched_P;
-  const int u = (unit % P.sched_P) * P.sched_R + (P.sched_R - 1 - slot % P.sched_R);
-  if (u >= P.nq) return;
-  const int b = bhi / P.Hq;
-  const int h = bhi % P.Hq;
-
+  const int qoff = P.queue_meta[xcd];
+  const int qcnt = P.queue_meta[8 + xcd];
   __shared__ __attribute__((aligned(16))) char smem_g[kSmem];
+  // the queue ticket shares the first word of the K ring: it is written and
+  // read between items, when no copy is in flight
+  int& s_next = *reinterpret_cast<int*>(smem_g);
   lds_char* smem = (lds_char*)smem_g;
-  const int kind = __builtin_amdgcn_readfirstlane(P.ht.kind[h]);
-  if (kind == MINF_VSLASH) attn_item<MINF_VSLASH>(P, b, h, u, slot, smem);
-  else if (kind == MINF_BSPARSE) attn_item<MINF_BSPARSE>(P, b, h, u, slot, smem);
-  else attn_item<MINF_ASHAPE>(P, b, h, u, slot, smem);
+  while (true) {
+    if (threadIdx.x == 0) s_next = atomicAdd(&P.queue_meta[16 + xcd], 1);
+    __syncthreads();
+    const int qi = __builtin_amdgcn_readfirstlane(s_next);
+    __syncthreads();   // both waves hold qi before the next write of s_next
+    if (qi >= qcnt) break;
+    const int item = ld_uniform(P.queue, (int64_t)qoff + qi);
+    const int bhi = item / P.nq;
+    const int u = item % P.nq;
+    const int b = bhi / P.Hq;
+    const int h = bhi % P.Hq;
+    const int kind = __builtin_amdgcn_readfirstlane(P.ht.kind[h]);
+    if (kind == MINF_VSLASH) attn_item<MINF_VSLASH>(P, b, h, u, qi, smem);
+    else if (kind == MINF_BSPARSE) attn_item<MINF_BSPARSE>(P, b, h, u, qi, smem);
+    else attn_item<MINF_ASHAPE>(P, b, h, u, qi, smem);
+    __syncthreads();   // the next item reuses the LDS rings
+  }
 }
 
 hipError_t launch_attn_bf16_d128(const AttnParams& p, hipStream_t st) {
-  const int units = p.B * p.Hq * p.sched_P;
-  const int upad = 8 * p.sched_per_xcd;
-  hipLaunchKernelGGL(attn_cost_kernel, dim3(upad), dim3(256), 0, st, p, units);
-  hipLaunchKernelGGL(attn_sched_kernel, dim3(1), dim3(256), 0, st, p, upad);
-  const unsigned grid = (unsigned)upad * (unsigned)p.sched_R;
-  hipLaunchKernelGGL(attn_bf16_d128_kernel, dim3(grid), dim3(128), 0, st, p);
+  static int wgs = 0;
+  if (!wgs) {
+    int dev = 0, cus = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e != hipSuccess) return e;
+    wgs = ((4 * cus + 7) / 8) * 8;   // four two-wave work-groups per CU
+  }
+  hipLaunchKernelGGL(attn_cost_kernel, dim3(p.sched_units), dim3(256), 0, st, p);
+  hipLaunchKernelGGL(attn_sched_kernel, dim3(1), dim3(256), 0, st, p);
+  hipLaunchKernelGGL(attn_fill_kernel, dim3(p.sched_units), dim3(256), 0, st, p);
+  hipLaunchKernelGGL(attn_bf16_d128_kernel, dim3(wgs), dim3(128), 0, st, p);
   return hipGetLastError();
 }
 

@@ -140,15 +140,18 @@ minf::VsWs vs_ws(const minf_problem* p, const Derived& d) {
   return minf::vs_workspace(p->B, p->Hq, p->n, (int)d.nq);
 }
 
-struct AttnWs { size_t cost, order, sched, total; int P, R, per_xcd; };
+struct AttnWs { size_t cost, order, uxcd, uoff, queue, meta, total; int P, R, units; };
 AttnWs attn_ws(const minf_problem* p, const Derived& d) {
   Carve c;
   AttnWs w;
-  minf::attn_sched_shape(p->B, p->Hq, d.nq, &w.P, &w.R, &w.per_xcd);
-  const size_t upad = 8 * (size_t)w.per_xcd;
-  w.cost = c.take(upad * 8);
-  w.order = c.take(upad * 4);
-  w.sched = c.take(upad * 4);
+  minf::attn_sched_shape(p->B, p->Hq, d.nq, &w.P, &w.R);
+  w.units = p->B * p->Hq * w.P;
+  w.cost = c.take((size_t)w.units * 8);
+  w.order = c.take((size_t)w.units * 4);
+  w.uxcd = c.take((size_t)w.units * 4);
+  w.uoff = c.take((size_t)w.units * 4);
+  w.queue = c.take((size_t)p->B * p->Hq * d.nq * 4);
+  w.meta = c.take(24 * 4);
   w.total = c.off;
   return w;
 }
@@ -292,10 +295,14 @@ minf_status minf_sparse_attn(const minf_problem* prob, const minf_head_cfg* head
   if ((s = check_ws(prob, d, ws, ws_bytes)) != MINF_OK) return s;
   const AttnWs w = attn_ws(prob, d);
   minf::AttnParams a{};
-  a.sched_cost = reinterpret_cast<int64_t*>(static_cast<char*>(ws) + w.cost);
-  a.sched_order = reinterpret_cast<int32_t*>(static_cast<char*>(ws) + w.order);
-  a.sched = reinterpret_cast<int32_t*>(static_cast<char*>(ws) + w.sched);
-  a.sched_P = w.P; a.sched_R = w.R; a.sched_per_xcd = w.per_xcd;
+  char* wb = static_cast<char*>(ws);
+  a.sched_cost = reinterpret_cast<int64_t*>(wb + w.cost);
+  a.sched_order = reinterpret_cast<int32_t*>(wb + w.order);
+  a.unit_xcd = reinterpret_cast<int32_t*>(wb + w.uxcd);
+  a.unit_off = reinterpret_cast<int32_t*>(wb + w.uoff);
+  a.queue = reinterpret_cast<int32_t*>(wb + w.queue);
+  a.queue_meta = reinterpret_cast<int32_t*>(wb + w.meta);
+  a.sched_P = w.P; a.sched_R = w.R; a.sched_units = w.units;
   a.Q = Q; a.K = K; a.V = V; a.O = O; a.lse = lse;
   a.blk_idx = blk_idx; a.blk_cnt = blk_cnt;
   if (d.has_vs) {

@@ -26,22 +26,24 @@ struct AttnParams {
   float c;          // scale * log2(e)
   int32_t out_bf16;
   HeadTable ht;     // ASHAPE: a = sink, b = window
-  // per-XCD schedule (attn_bf16.hip): units are (b*Hq + h) * sched_P + part,
+  // per-XCD work queues (attn_bf16.hip); units are (b*Hq + h) * sched_P + part,
   // part covering query blocks [part*sched_R, (part+1)*sched_R)
-  int64_t* sched_cost;      // ws [8 * sched_per_xcd]
-  int32_t* sched_order;     // ws [8 * sched_per_xcd]
-  int32_t* sched;           // ws [8][sched_per_xcd], -1 = empty
-  int32_t sched_P, sched_R, sched_per_xcd;
+  int64_t* sched_cost;      // ws [sched_units]
+  int32_t* sched_order;     // ws [sched_units]
+  int32_t* unit_xcd;        // ws [sched_units], -1 = no items
+  int32_t* unit_off;        // ws [sched_units]: first item within its XCD's queue
+  int32_t* queue;           // ws [B*Hq*nq]: items b*Hq*nq + h*nq + u
+  int32_t* queue_meta;      // ws [24]: queue offsets, counts, counters per XCD
+  int32_t sched_P, sched_R, sched_units;
 };
 // Units of the attention schedule for B*Hq heads and nq query blocks.
-inline void attn_sched_shape(int B, int Hq, int64_t nq, int* P, int* R, int* per_xcd) {
+inline void attn_sched_shape(int B, int Hq, int64_t nq, int* P, int* R) {
   const int bh = B * Hq;
   int parts = bh >= 32 ? 1 : (32 + bh - 1) / bh;
   if (parts > nq) parts = (int)nq;
   if (parts < 1) parts = 1;
   *P = parts;
   *R = (int)((nq + parts - 1) / parts);
-  *per_xcd = (bh * parts + 7) / 8;
 }
 hipError_t launch_attn(const AttnParams& p, int in_bf16, int dh, hipStream_t st);
 // bf16 inputs with dh = 128 (attn_bf16.hip)
