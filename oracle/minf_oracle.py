@@ -272,6 +272,56 @@ def attend_rows(q, k, v, rows: np.ndarray, mask_fn: Callable, scale: float, chun
 
 
 # ----------------------------------------------------------------------------
+# one row at a time: the candidate keys of row i listed explicitly, and the
+# restricted softmax over them.  For long sequences, where a dense mask of
+# many rows against all keys does not fit; same definitions as above.
+# ----------------------------------------------------------------------------
+
+def ashape_row_keys(i: int, sink: int, window: int) -> np.ndarray:
+    """N(i) of Eq. 3, ascending: [0, min(g-1, i)] united with [max(0, i-w+1), i]."""
+    j = np.arange(i + 1, dtype=np.int64)
+    return j[(j < sink) | (j >= i - window + 1)]
+
+
+def vs_row_keys(i: int, cols, cover: np.ndarray, slash_tile: int) -> np.ndarray:
+    """N(i) of the VS set, ascending: keys j <= i of row i's query block
+    u = i // t that a slash covers (t*u - j in S, `cover` from
+    slash_offset_set), united with the columns j <= i."""
+    t = slash_tile
+    u = i // t
+    x = np.nonzero(cover)[0] - (t - 1)             # the covered offsets x
+    j = t * u - x
+    j = j[(j >= 0) & (j <= i)]
+    c = np.asarray(cols, dtype=np.int64)
+    c = c[c <= i]
+    return np.union1d(j, c)
+
+
+def bs_row_keys(i: int, J: Sequence[np.ndarray], block: int = BLOCK) -> np.ndarray:
+    """N(i) of Eq. 6, ascending: keys j <= i whose block is in J_{i // block}."""
+    out = []
+    for v in np.sort(np.asarray(J[i // block], dtype=np.int64)):
+        lo = v * block
+        hi = min(lo + block - 1, i)
+        if lo <= hi:
+            out.append(np.arange(lo, hi + 1, dtype=np.int64))
+    return np.concatenate(out) if out else np.zeros(0, dtype=np.int64)
+
+
+def attend_row_keys(q_i: np.ndarray, k: np.ndarray, v: np.ndarray, keys: np.ndarray, scale: float):
+    """o_i and LSE_i of Eq. 2 over the listed keys: the softmax of
+    scale * q_i . k_j over j in keys, applied to v_j (o = 0, LSE = -inf when
+    the list is empty)."""
+    if keys.shape[0] == 0:
+        return np.zeros(v.shape[1]), -np.inf
+    s = scale * (k[keys] @ q_i)
+    m = s.max()
+    p = np.exp(s - m)
+    l = p.sum()
+    return (p @ v[keys]) / l, m + math.log(l)
+
+
+# ----------------------------------------------------------------------------
 # kept edges E_h = sum_i |N_h(i)|  ([MInf] section 1.2)
 # ----------------------------------------------------------------------------
 

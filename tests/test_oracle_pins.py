@@ -284,3 +284,42 @@ def test_slash_tile_one_is_eq5_and_64_is_spans():
         for d in offs:
             span |= {j for j in range(64 * u - d, 64 * u + 64 - d) if 0 <= j <= i}
         assert set(np.nonzero(m64[i])[0].tolist()) == span
+
+
+def test_row_key_lists_equal_masks_and_row_softmax_equals_attend_rows():
+    """The per-row candidate lists (used at long sequence lengths) against the
+    dense masks of Eq. 3, 5 and 6, and the per-row softmax against
+    attend_rows, on a small problem with ragged n, sinks, windows, slashes
+    that run past the start, and forced blocks."""
+    rng = np.random.default_rng(11)
+    n, dh = 203, 16
+    q, k, v = (rng.standard_normal((n, dh)) for _ in range(3))
+    sc = 0.3
+    rows = np.arange(n)
+    # A-shape
+    for g, w in [(0, 1), (5, 17), (64, 300), (3, 0)]:
+        m = O.ashape_mask(rows, n, g, w)
+        for i in (0, 1, 4, 5, 63, 64, 130, 202):
+            assert np.array_equal(O.ashape_row_keys(i, g, w), np.nonzero(m[i])[0])
+    # Vertical-Slash, both slash readings
+    cols = np.sort(rng.choice(n, 17, replace=False))
+    offs = np.sort(rng.choice(n, 9, replace=False))
+    for t in (64, 1):
+        cover = O.slash_offset_set(offs, n, t)
+        m = O.vs_mask(rows, n, n, cols, offs, t, cover)
+        for i in range(n):
+            assert np.array_equal(O.vs_row_keys(i, cols, cover, t), np.nonzero(m[i])[0]), (t, i)
+        # row softmax over the list equals the dense restricted softmax
+        ref_o, ref_l = O.attend_rows(q, k, v, rows, lambda r, nk: O.vs_mask(r, nk, n, cols, offs, t, cover), sc)
+        for i in (0, 7, 64, 150, 202):
+            o, l = O.attend_row_keys(q[i], k, v, O.vs_row_keys(i, cols, cover, t), sc)
+            assert np.allclose(o, ref_o[i], atol=1e-12) and np.isclose(l, ref_l[i])
+    # Block-Sparse with forced blocks and a block list that skips the diagonal
+    J = O.bs_index(q, k, 2, O.FORCE_FIRST_BLOCK, sc)
+    J[3] = np.array([0, 1])
+    m = O.bs_mask(rows, n, J)
+    for i in range(n):
+        assert np.array_equal(O.bs_row_keys(i, J), np.nonzero(m[i])[0]), i
+    # an empty list gives o = 0, LSE = -inf
+    o, l = O.attend_row_keys(q[5], k, v, np.zeros(0, dtype=np.int64), sc)
+    assert np.all(o == 0) and l == -np.inf
