@@ -25,8 +25,14 @@ struct BsBatch {
 };
 
 // grid (nq, B*Hq + B*Hkv): mean of each 64-row block of Q (BS heads) and K.
+// Thread t reads 16 bytes (columns 16/sizeof(T) * (t % CPR) ..) of rows
+// t / CPR, + RG, ...; the row groups are then summed through LDS in a fixed
+// order.
 template <typename T, int DH>
-__global__ __launch_bounds__(DH) void bs_pool_kernel(BsParams P, uint64_t kv_used) {
+__global__ __launch_bounds__(256) void bs_pool_kernel(BsParams P, uint64_t kv_used) {
+  constexpr int EPL = 16 / (int)sizeof(T);   // elements per 16-byte load
+  constexpr int CPR = DH / EPL;              // loads per row
+  constexpr int RG = 256 / CPR;              // row groups
   const int u = blockIdx.x;
   const int y = blockIdx.y;
   const int BHq = P.B * P.Hq;
@@ -45,13 +51,35 @@ __global__ __launch_bounds__(DH) void bs_pool_kernel(BsParams P, uint64_t kv_use
     dst = P.kbar + ((size_t)z * P.nq + u) * DH;
   }
   const int r0 = 64 * u, r1 = min(r0 + 64, P.n);
-  const int d = threadIdx.x;
-  float acc = 0.f;
-  for (int r = r0; r < r1; ++r) {
-    if constexpr (sizeof(T) == 2) acc += bf16_to_f32(src[(size_t)r * DH + d]);
-    else acc += src[(size_t)r * DH + d];
+  const int c = threadIdx.x % CPR, rg = threadIdx.x / CPR;
+  float acc[EPL];
+  #pragma unroll
+  for (int e = 0; e < EPL; ++e) acc[e] = 0.f;
+  for (int r = r0 + rg; r < r1; r += RG) {
+    if constexpr (sizeof(T) == 2) {
+      // the four packed dwords are read as separate scalars (bit-casting
+      // elements extracted from a loaded vector has been miscompiled)
+      const uint32_t* w = reinterpret_cast<const uint32_t*>(src + (size_t)r * DH + c * EPL);
+      const uint32_t w0 = w[0], w1 = w[1], w2 = w[2], w3 = w[3];
+      acc[0] += __builtin_bit_cast(float, w0 << 16); acc[1] += __builtin_bit_cast(float, w0 & 0xffff0000u);
+      acc[2] += __builtin_bit_cast(float, w1 << 16); acc[3] += __builtin_bit_cast(float, w1 & 0xffff0000u);
+      acc[4] += __builtin_bit_cast(float, w2 << 16); acc[5] += __builtin_bit_cast(float, w2 & 0xffff0000u);
+      acc[6] += __builtin_bit_cast(float, w3 << 16); acc[7] += __builtin_bit_cast(float, w3 & 0xffff0000u);
+    } else {
+      const floatx4 x = *reinterpret_cast<const floatx4*>(src + (size_t)r * DH + c * EPL);
+      #pragma unroll
+      for (int e = 0; e < 4; ++e) acc[e] += x[e];
+    }
   }
-  dst[d] = acc / (float)(r1 - r0);
+  __shared__ float part[RG][DH + 1];
+  #pragma unroll
+  for (int e = 0; e < EPL; ++e) part[rg][c * EPL + e] = acc[e];
+  __syncthreads();
+  if ((int)threadIdx.x < DH) {
+    float sum = 0.f;
+    for (int g = 0; g < RG; ++g) sum += part[g][threadIdx.x];
+    dst[threadIdx.x] = sum / (float)(r1 - r0);
+  }
 }
 
 // grid (tiles_v, tiles_u, batch): 64x64 causal tiles of R = scale * Qbar Kbar^T.
@@ -100,18 +128,20 @@ __global__ __launch_bounds__(256) void bs_score_kernel(BsParams P, BsBatch batch
   }
 }
 
-// grid (nq, batch): exact top-k of row u over v <= u.
+// grid (nq, batch): exact top-k of row u over v <= u, the row held in
+// registers (E = ceil(nq / 256) scores per thread).
+template <int E>
 __global__ __launch_bounds__(256) void bs_topk_kernel(BsParams P, BsBatch batch) {
   const int u = blockIdx.x;
   const int bh = batch.bh[blockIdx.y];
   const int h = bh % P.Hq;
-  __shared__ TopkShared sh;
+  __shared__ TopkRegShared sh;
   const float* row = P.scores + ((size_t)blockIdx.y * P.nq + u) * P.nq;
   const int force = P.ht.b[h];
   const float inf = __builtin_huge_valf();
   const int k = min(P.ht.a[h], u + 1);
   int32_t* out = P.blk_idx + ((size_t)bh * P.nq + u) * P.max_kb;
-  block_topk<256, 8>(
+  block_topk_reg<256, E>(
       [&](int v) {
         if (((force & MINF_FORCE_FIRST_BLOCK) && v == 0) || ((force & MINF_FORCE_DIAG_BLOCK) && v == u)) return inf;
         return row[v];
@@ -120,18 +150,29 @@ __global__ __launch_bounds__(256) void bs_topk_kernel(BsParams P, BsBatch batch)
   if (threadIdx.x == 0) P.blk_cnt[(size_t)bh * P.nq + u] = k;
 }
 
+template <int E>
+static void launch_topk(const BsParams& p, const BsBatch& batch, hipStream_t st) {
+  hipLaunchKernelGGL(bs_topk_kernel<E>, dim3(p.nq, batch.count), dim3(256), 0, st, p, batch);
+}
+
 template <typename T, int DH>
 hipError_t launch_t(const BsParams& p, hipStream_t st) {
   uint64_t kv_used = 0;
   for (int h = 0; h < p.Hq; ++h)
     if (p.ht.kind[h] == MINF_BSPARSE) kv_used |= 1ull << (h / (p.Hq / p.Hkv));
-  hipLaunchKernelGGL((bs_pool_kernel<T, DH>), dim3(p.nq, p.B * (p.Hq + p.Hkv)), dim3(DH), 0, st, p, kv_used);
+  hipLaunchKernelGGL((bs_pool_kernel<T, DH>), dim3(p.nq, p.B * (p.Hq + p.Hkv)), dim3(256), 0, st, p, kv_used);
   BsBatch batch{};
   const int tiles = (p.nq + 63) / 64;
   auto flush = [&]() {
     if (!batch.count) return;
     hipLaunchKernelGGL((bs_score_kernel<DH>), dim3(tiles, tiles, batch.count), dim3(256), 0, st, p, batch);
-    hipLaunchKernelGGL(bs_topk_kernel, dim3(p.nq, batch.count), dim3(256), 0, st, p, batch);
+    const int64_t per = (p.nq + 255) / 256;   // scores per thread
+    if (per <= 4) launch_topk<4>(p, batch, st);
+    else if (per <= 8) launch_topk<8>(p, batch, st);
+    else if (per <= 16) launch_topk<16>(p, batch, st);
+    else if (per <= 32) launch_topk<32>(p, batch, st);
+    else if (per <= 64) launch_topk<64>(p, batch, st);
+    else launch_topk<128>(p, batch, st);
     batch.count = 0;
   };
   const int cap = (int)std::min<int64_t>(p.score_heads, 64);

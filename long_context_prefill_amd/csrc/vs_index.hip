@@ -86,22 +86,25 @@ struct ProxyOps {
 
 // PASS 1: per-row running (max, sum) partials.  PASS 2: probabilities,
 // column sums and diagonal partials.
+// grid (key ranges, B*Hq): one work-group per 1024 consecutive keys of one
+// query head; the ranges of a head are dispatched in order.
 template <typename T, int DH, int PASS>
 __global__ __launch_bounds__(256) void vs_proxy_kernel(VsParams P) {
   using Ops = ProxyOps<T, DH>;
+  const int gsz = P.Hq / P.Hkv;
   const int bh = blockIdx.y;
+  const int range = blockIdx.x;
   const int h = bh % P.Hq;
   if (P.ht.kind[h] != MINF_VSLASH) return;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int r16 = lane & 15, g = lane >> 4;
   const int n = P.n;
   const int L = min(P.ht.a[h], n);
-  const int gsz = P.Hq / P.Hkv;
   const int b = bh / P.Hq;
   const int kv = h / gsz;
   const T* Qb = reinterpret_cast<const T*>(P.Q) + (size_t)bh * n * DH;
   const T* Kb = reinterpret_cast<const T*>(P.K) + ((size_t)b * P.Hkv + kv) * n * DH;
-  const int slot = blockIdx.x * 4 + wave;
+  const int slot = range * 4 + wave;
   const int J0 = slot * kVsWaveKeys;
   const int J1 = min(J0 + kVsWaveKeys, n);
   const int row_base = n - L;    // sampled row r is query n - L + r (valid for r < L)
@@ -256,22 +259,31 @@ __global__ __launch_bounds__(256) void vs_proxy_kernel(VsParams P) {
   }
 }
 
-// LSE of every sampled row from the per-wave partials (fixed order).
-__global__ __launch_bounds__(64) void vs_lse_kernel(VsParams P, int nslots_used) {
-  const int bh = blockIdx.x;
+// LSE of every sampled row from the per-wave partials: one wave per row,
+// lane l folds the partials l, l+64, ... (a fixed order), then the lanes are
+// combined by a fixed butterfly.
+__global__ __launch_bounds__(256) void vs_lse_kernel(VsParams P, int nslots_used) {
+  const int bh = blockIdx.y;
   const int h = bh % P.Hq;
   if (P.ht.kind[h] != MINF_VSLASH) return;
-  const int r = threadIdx.x;
+  const int lane = threadIdx.x & 63;
+  const int r = blockIdx.x * 4 + (threadIdx.x >> 6);
   const float* pm = reinterpret_cast<const float*>(P.ws_base + P.ws.part_m) + ((size_t)bh * 64 + r) * P.ws.nslots;
   const float* pl = reinterpret_cast<const float*>(P.ws_base + P.ws.part_l) + ((size_t)bh * 64 + r) * P.ws.nslots;
   float M = kNegInf;
-  for (int s = 0; s < nslots_used; ++s) M = fmaxf(M, pm[s]);
+  for (int s = lane; s < nslots_used; s += 64) M = fmaxf(M, pm[s]);
+  #pragma unroll
+  for (int off = 32; off > 0; off >>= 1) M = fmaxf(M, __shfl_xor(M, off));
   float Lsum = 0.f;
   if (M != kNegInf)
-    for (int s = 0; s < nslots_used; ++s) Lsum += fast_exp2(pm[s] - M) * pl[s];
-  float* l2 = reinterpret_cast<float*>(P.ws_base + P.ws.lse2) + (size_t)bh * 64;
-  // rows without any key (r >= L) get +inf so that their probabilities are 0
-  l2[r] = (Lsum > 0.f) ? M + __log2f(Lsum) : __builtin_huge_valf();
+    for (int s = lane; s < nslots_used; s += 64) Lsum += fast_exp2(pm[s] - M) * pl[s];
+  #pragma unroll
+  for (int off = 32; off > 0; off >>= 1) Lsum += __shfl_xor(Lsum, off);
+  if (lane == 0) {
+    float* l2 = reinterpret_cast<float*>(P.ws_base + P.ws.lse2) + (size_t)bh * 64;
+    // rows without any key (r >= L) get +inf so that their probabilities are 0
+    l2[r] = (Lsum > 0.f) ? M + __log2f(Lsum) : __builtin_huge_valf();
+  }
 }
 
 // r_d = sum of the (at most two) wave partials whose keys can form offset d.
@@ -317,7 +329,7 @@ __global__ __launch_bounds__(1024) void vs_topk_kernel(VsParams P) {
     k = P.ht.c[h];
     cap = (int)P.max_s;
   }
-  block_topk<1024, 16>([&](int i) { return src[i]; }, n, k, out, cap, sh);
+  block_topk_array<1024>(src, n, k, out, cap, sh);
 }
 
 template <typename T, int DH>
@@ -325,7 +337,7 @@ hipError_t launch_t(const VsParams& p, hipStream_t st) {
   const unsigned BH = (unsigned)(p.B * p.Hq);
   const unsigned nwg = (unsigned)((p.n + kVsGroupKeys - 1) / kVsGroupKeys);
   hipLaunchKernelGGL((vs_proxy_kernel<T, DH, 1>), dim3(nwg, BH), dim3(256), 0, st, p);
-  hipLaunchKernelGGL(vs_lse_kernel, dim3(BH), dim3(64), 0, st, p, (int)(nwg * 4));
+  hipLaunchKernelGGL(vs_lse_kernel, dim3(16, BH), dim3(256), 0, st, p, (int)(nwg * 4));
   hipLaunchKernelGGL((vs_proxy_kernel<T, DH, 2>), dim3(nwg, BH), dim3(256), 0, st, p);
   hipLaunchKernelGGL(vs_diag_kernel, dim3((p.n + 255) / 256, BH), dim3(256), 0, st, p);
   hipLaunchKernelGGL(vs_topk_kernel, dim3(2 * BH), dim3(1024), 0, st, p);
