@@ -27,17 +27,18 @@ METRIC = "sparse prefill ms/layer @128K (index+attn) and kept-edge TFLOP/s vs bf
 PEAK_BF16_TFLOPS = 2500.0        # MI355X dense bf16 matrix peak
 PEAK_HBM_GBS = 8000.0            # MI355X HBM3E
 
-# HBM traffic of one attention launch on the 128K mixed layer, from two
-# rocprofv3 --pmc runs of this script (FETCH_SIZE, then WRITE_SIZE, KiB per
-# dispatch), each scaled by what the same counter reads for a plain device
-# copy of known size (bench.py --copy-mib).  Valid only for the kernel
-# sources they were taken from: the hash covers them, and a mismatch reports
-# null.
-ATTN_SOURCES = ["long_context_prefill_amd/csrc/attn.hip", "long_context_prefill_amd/csrc/common.h",
-                "long_context_prefill_amd/csrc/kernels.h"]
-ATTN_TRAFFIC = {"workload": "n128k_h32kv8_d128_bf16_mixed", "sources": "6d6a48e95a860a70",
-                "fetch_kib": 50494062.7, "fetch_factor": 1048576 / 524304.6,
-                "write_kib": 2097152.0, "write_factor": 1048576 / 1048576.0}
+# HBM traffic of one attention-kernel launch on the 128K mixed layer, from
+# two rocprofv3 --pmc runs of this script (FETCH_SIZE, then WRITE_SIZE, KiB
+# per dispatch), each scaled by what the same counter reads for a plain
+# device copy of known size (bench.py --copy-mib).  Valid only for the kernel
+# sources they were taken from: the hash covers them, and a mismatch (or
+# None) reports null.
+ATTN_KERNEL = "attn_bf16_d128_kernel"
+ATTN_SOURCES = ["long_context_prefill_amd/csrc/attn_bf16.hip", "long_context_prefill_amd/csrc/common.h",
+                "long_context_prefill_amd/csrc/kernels.h", "include/minf.h"]
+ATTN_TRAFFIC = {"workload": "n128k_h32kv8_d128_bf16_mixed", "sources": "6af336a46046500b",
+                "fetch_kib": 84134387.25, "fetch_factor": 1048576 / 524304.65,
+                "write_kib": 2102126.9, "write_factor": 1048576 / 1048576.0}
 
 
 def log(*a):
@@ -177,6 +178,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-flush", action="store_true",
+                    help="skip the 1 GiB cache-flushing write before each timed step")
     ap.add_argument("--out-dtype", default="f32", choices=["f32", "bf16"])
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="only run a plain device copy of this many MiB (memory-counter calibration)")
@@ -233,24 +236,43 @@ def main():
     if int(t["status"].item()) != 0:
         raise RuntimeError(f"device status {int(t['status'].item())}")
 
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(a.steps)]
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for s in range(a.steps):
-        step(evs[s])
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    ms_step = 1000.0 * wall / a.steps
-    st = {k: 0.0 for k in stages}
-    for s in range(a.steps):
-        for i, k in enumerate(stages):
-            st[k] += evs[s][i].elapsed_time(evs[s][i + 1]) / a.steps
-    ms_index = st["vs_index"] + st["bs_index"] + st["build_tiles"]
+    # Timed steps.  Before each one a 1 GiB write evicts L2 and the MALL
+    # (outside the events), so the layer starts with cold caches, as it would
+    # after the projections of a real layer.  The events bracket each call;
+    # the library's own event pair brackets the attention kernel alone.
+    flush = None if a.no_flush else torch.empty(1 << 28, dtype=torch.float32, device="cuda")
+
+    def timed(k, do_flush):
+        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(k)]
+        M.minf_timing_start(k)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for s_ in range(k):
+            if do_flush:
+                flush.fill_(float(s_))
+            step(evs[s_])
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        kern = M.minf_timing_read(k)
+        per = [[evs[s_][i].elapsed_time(evs[s_][i + 1]) for i in range(4)] for s_ in range(k)]
+        return wall, per, kern
+
+    wall, per, kern = timed(a.steps, flush is not None)
+    if int(t["status"].item()) != 0:
+        raise RuntimeError(f"device status {int(t['status'].item())}")
+    warm = timed(a.steps, False)[1] if flush is not None else None
+    ms_wall = 1000.0 * wall / a.steps
+    layer = np.array([sum(x) for x in per])
+    st = {k: float(np.median([x[i] for x in per])) for i, k in enumerate(stages)}
+    ms_step = float(np.median(layer))
+    ms_index = float(np.median([x[0] + x[1] + x[2] for x in per]))
     ms_attn = st["sparse_attn"]
+    ms_kernel = float(np.mean(kern))
 
     kept = int(t["kept_edges"].sum().item())
     flops = 4.0 * p.dh * kept * p.B if p.B == 1 else 4.0 * p.dh * kept
     attn_tflops = flops / (ms_attn * 1e-3) / 1e12
+    kern_tflops = flops / (ms_kernel * 1e-3) / 1e12
     ib = index_bytes(p)
     idx_gbs = ib / (ms_index * 1e-3) / 1e9
     per_kind = {}
@@ -278,7 +300,7 @@ def main():
         "n_gpus": 1,
         "steps": a.steps,
         "warmup": a.warmup,
-        "ms_per_step": round(ms_step, 3),
+        "ms_per_step": round(ms_wall, 3),
         "higher_is_better": False,
         "scaling": "weak",
         "vs_baseline": None,
@@ -288,6 +310,11 @@ def main():
                    "heads": "16 vertical-slash (64/1000/6096), 8 block-sparse (top-100), 8 A-shape (128/4096)"
                    if a.workload == 3 else str(sorted(per_kind)),
                    "out_dtype": a.out_dtype},
+        "timing": ("median over the timed steps of the event-timed layer (index + attention); "
+                   + ("each step starts after a 1 GiB cache-flushing write, which ms_per_step (wall clock) "
+                      "includes" if flush is not None else "warm caches")),
+        "ms_layer_min_max": [round(float(layer.min()), 3), round(float(layer.max()), 3)],
+        "ms_layer_warm": round(float(np.median([sum(x) for x in warm])), 3) if warm else None,
         "stages_ms": {k: round(v, 4) for k, v in st.items()},
         "ms_index": round(ms_index, 4),
         "ms_attn": round(ms_attn, 4),
@@ -300,11 +327,12 @@ def main():
         "frac_bf16_peak": round(attn_tflops / PEAK_BF16_TFLOPS, 4),
         "index_gbs": round(idx_gbs, 1),
         "index_frac_hbm": round(idx_gbs / PEAK_HBM_GBS, 4),
-        "roofline": {"bound": "mfma", "achieved": round(attn_tflops, 2), "peak": PEAK_BF16_TFLOPS,
-                     "unit": "TFLOP/s", "frac": round(attn_tflops / PEAK_BF16_TFLOPS, 4),
-                     "traffic": attn_traffic(p.name), "traffic_unit": "bytes per launch",
-                     "kernel": "attn_kernel<bf16,128> (minf_sparse_attn)",
-                     "per_launch_flops": flops, "avg_launch_ms": round(ms_attn, 4)},
+        "roofline": {"bound": "mfma", "achieved": round(kern_tflops, 2), "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(kern_tflops / PEAK_BF16_TFLOPS, 4),
+                     "traffic": attn_traffic(p.name), "traffic_unit": "HBM bytes per launch",
+                     "kernel": ATTN_KERNEL if (p.dtype == "bf16" and p.dh == 128) else "attn_kernel",
+                     "per_launch_flops": flops, "avg_launch_ms": round(ms_kernel, 4),
+                     "launches_timed": len(kern)},
         "cpu_baseline": cpu,
         "context": "pages: up to 10x prefill speedup over dense on an A100 (another machine and workload)",
     }

@@ -216,6 +216,21 @@ minf_status minf_sparse_attn(const minf_problem* prob, const minf_head_cfg* head
                              void* O, float* lse,
                              void* ws, size_t ws_bytes, void* stream);
 
+/* Kernel timing, for measurement harnesses; computing never needs it.
+ * After minf_timing_start(max_calls), each of the next max_calls calls of
+ * minf_sparse_attn records a HIP event pair on its stream around its main
+ * attention kernel only (the work-item scheduling kernels before it are
+ * outside the pair).  Later calls record nothing.  The library owns the
+ * events: start creates them (replacing any from an earlier start, unread),
+ * read releases them.  max_calls must lie in [1, 65536] (else MINF_EINVAL);
+ * MINF_EHIP if an event cannot be created.
+ * minf_timing_read waits on the host for the recorded pairs, writes the
+ * first min(recorded, cap) durations in milliseconds to ms[] (host memory),
+ * sets *count to the number of recorded pairs and ends the timing.  Not
+ * thread safe: one timing at a time per process. */
+minf_status minf_timing_start(int32_t max_calls);
+minf_status minf_timing_read(float* ms, int32_t cap, int32_t* count);
+
 const char* minf_status_string(minf_status s);
 /* Message of the last failed call on this thread ("" if none). */
 const char* minf_last_error(void);

@@ -29,7 +29,8 @@ MINF_FORCE_FIRST_BLOCK, MINF_FORCE_DIAG_BLOCK = 1, 2
 MINF_DEV_BAD_VERTICAL, MINF_DEV_BAD_SLASH, MINF_DEV_BAD_BLOCK, MINF_DEV_CAPACITY = 1, 2, 4, 8
 
 EXPORTED = ["minf_query_sizes", "minf_vs_index", "minf_bs_index", "minf_build_tiles",
-            "minf_sparse_attn", "minf_status_string", "minf_last_error", "minf_version"]
+            "minf_sparse_attn", "minf_timing_start", "minf_timing_read", "minf_status_string",
+            "minf_last_error", "minf_version"]
 
 
 class MinfError(RuntimeError):
@@ -85,6 +86,10 @@ def load_library(path: str = LIB_PATH):
                                      vp, ctypes.c_size_t, vp]
     for f in ("minf_query_sizes", "minf_vs_index", "minf_bs_index", "minf_build_tiles", "minf_sparse_attn"):
         getattr(lib, f).restype = ctypes.c_int
+    lib.minf_timing_start.argtypes = [ctypes.c_int32]
+    lib.minf_timing_start.restype = ctypes.c_int
+    lib.minf_timing_read.argtypes = [P(ctypes.c_float), ctypes.c_int32, P(ctypes.c_int32)]
+    lib.minf_timing_read.restype = ctypes.c_int
     lib.minf_status_string.argtypes = [ctypes.c_int]
     lib.minf_status_string.restype = ctypes.c_char_p
     lib.minf_last_error.argtypes = []
@@ -180,6 +185,21 @@ def minf_sparse_attn(prob, heads, Q, K, V, blk_idx, blk_cnt, tiles: Optional[dic
     _check(lib.minf_sparse_attn(ctypes.byref(prob), heads, _ptr(Q), _ptr(K), _ptr(V), _ptr(blk_idx),
                                 _ptr(blk_cnt), ctypes.byref(ts), _ptr(O), _ptr(lse), _ptr(ws), _nbytes(ws),
                                 _stream(stream)))
+
+
+def minf_timing_start(max_calls: int):
+    lib = load_library()
+    _check(lib.minf_timing_start(int(max_calls)))
+
+
+def minf_timing_read(cap: int) -> list:
+    """Durations (ms) of the main attention kernel of the sparse-attention
+    calls made since minf_timing_start, in call order."""
+    lib = load_library()
+    arr = (ctypes.c_float * max(1, cap))()
+    cnt = ctypes.c_int32(0)
+    _check(lib.minf_timing_read(arr, int(cap), ctypes.byref(cnt)))
+    return [float(arr[i]) for i in range(min(cap, cnt.value))]
 
 
 # ---------------------------------------------------------------- buffers

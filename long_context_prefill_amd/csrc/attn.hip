@@ -573,7 +573,9 @@ static hipError_t launch_t(const AttnParams& p, hipStream_t st) {
     if (e != hipSuccess) return e;
     attr_set = true;
   }
+  timing_mark(st, 0);
   hipLaunchKernelGGL((attn_kernel<T, DH>), dim3(grid), dim3(256), smem, st, p);
+  timing_mark(st, 1);
   return hipGetLastError();
 }
 

@@ -731,7 +731,9 @@ hipError_t launch_attn_bf16_d128(const AttnParams& p, hipStream_t st) {
   hipLaunchKernelGGL(attn_cost_kernel, dim3(p.sched_units), dim3(256), 0, st, p);
   hipLaunchKernelGGL(attn_sched_kernel, dim3(1), dim3(256), 0, st, p);
   hipLaunchKernelGGL(attn_fill_kernel, dim3(p.sched_units), dim3(256), 0, st, p);
+  timing_mark(st, 0);
   hipLaunchKernelGGL(attn_bf16_d128_kernel, dim3(wgs), dim3(128), 0, st, p);
+  timing_mark(st, 1);
   return hipGetLastError();
 }
 

@@ -7,6 +7,7 @@
 #include <string.h>
 
 #include <algorithm>
+#include <vector>
 
 #include "common.h"
 #include "kernels.h"
@@ -175,7 +176,32 @@ minf_status hip_status(hipError_t e, const char* what) {
   return fail(MINF_EHIP, "%s: %s", what, hipGetErrorString(e));
 }
 
+// Event pairs of minf_timing_start() / minf_timing_read(): pair i brackets
+// the main attention kernel of the i-th minf_sparse_attn call since the start.
+struct Timing {
+  std::vector<hipEvent_t> ev;   // 2 * cap events: start, end, start, end, ...
+  int cap = 0, used = 0;
+  hipError_t err = hipSuccess;
+};
+Timing g_timing;
+
+void timing_release() {
+  for (hipEvent_t e : g_timing.ev) (void)hipEventDestroy(e);
+  g_timing = Timing{};
+}
+
 }  // namespace
+
+namespace minf {
+
+void timing_mark(hipStream_t st, int end) {
+  if (g_timing.used >= g_timing.cap) return;
+  const hipError_t e = hipEventRecord(g_timing.ev[2 * g_timing.used + end], st);
+  if (e != hipSuccess && g_timing.err == hipSuccess) g_timing.err = e;
+  if (end) ++g_timing.used;
+}
+
+}  // namespace minf
 
 extern "C" {
 
@@ -319,6 +345,38 @@ minf_status minf_sparse_attn(const minf_problem* prob, const minf_head_cfg* head
   a.ht = d.ht;
   return hip_status(minf::launch_attn(a, prob->in_dtype == MINF_BF16, prob->dh, static_cast<hipStream_t>(stream)),
                     "minf_sparse_attn launch");
+}
+
+minf_status minf_timing_start(int32_t max_calls) {
+  if (max_calls < 1 || max_calls > 65536) return fail(MINF_EINVAL, "max_calls %d outside [1, 65536]", max_calls);
+  timing_release();
+  std::vector<hipEvent_t> ev(2 * (size_t)max_calls, nullptr);
+  for (size_t i = 0; i < ev.size(); ++i) {
+    const hipError_t e = hipEventCreate(&ev[i]);
+    if (e != hipSuccess) {
+      for (size_t j = 0; j < i; ++j) (void)hipEventDestroy(ev[j]);
+      return hip_status(e, "minf_timing_start: hipEventCreate");
+    }
+  }
+  g_timing.ev = std::move(ev);
+  g_timing.cap = max_calls;
+  return MINF_OK;
+}
+
+minf_status minf_timing_read(float* ms, int32_t cap, int32_t* count) {
+  if (!count || (cap > 0 && !ms) || cap < 0) return fail(MINF_EINVAL, "null count or output array");
+  if (g_timing.cap == 0) return fail(MINF_EINVAL, "minf_timing_start was not called");
+  minf_status s = hip_status(g_timing.err, "minf_timing: hipEventRecord");
+  const int used = g_timing.used;
+  for (int i = 0; s == MINF_OK && i < used && i < cap; ++i) {
+    s = hip_status(hipEventSynchronize(g_timing.ev[2 * i + 1]), "minf_timing_read: hipEventSynchronize");
+    if (s == MINF_OK)
+      s = hip_status(hipEventElapsedTime(&ms[i], g_timing.ev[2 * i], g_timing.ev[2 * i + 1]),
+                     "minf_timing_read: hipEventElapsedTime");
+  }
+  *count = used;
+  timing_release();
+  return s;
 }
 
 }  // extern "C"

@@ -48,6 +48,9 @@ inline void attn_sched_shape(int B, int Hq, int64_t nq, int* P, int* R) {
 hipError_t launch_attn(const AttnParams& p, int in_bf16, int dh, hipStream_t st);
 // bf16 inputs with dh = 128 (attn_bf16.hip)
 hipError_t launch_attn_bf16_d128(const AttnParams& p, hipStream_t st);
+// Records the start (end = 0) or end (end = 1) event of the main attention
+// kernel on st while minf_timing_start() is in effect; a no-op otherwise.
+void timing_mark(hipStream_t st, int end);
 size_t attn_smem_bytes(int dh);
 
 // ---------------------------------------------------------------- tiles

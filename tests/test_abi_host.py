@@ -115,3 +115,13 @@ def test_no_work_for_absent_kinds(lib):
     h = M.make_heads([gen.ashape(4, 8)] * 4)
     assert lib.minf_vs_index(ctypes.byref(p), h, None, None, None, None, None, None, None, 0, None) == M.MINF_OK
     assert lib.minf_bs_index(ctypes.byref(p), h, None, None, None, None, None, 0, None) == M.MINF_OK
+
+
+def test_timing_rejects_bad_arguments(lib):
+    # argument checks answer before any event is created
+    assert lib.minf_timing_start(0) == M.MINF_EINVAL
+    assert lib.minf_timing_start(65537) == M.MINF_EINVAL
+    cnt = ctypes.c_int32(-1)
+    assert lib.minf_timing_read(None, 0, ctypes.byref(cnt)) == M.MINF_EINVAL   # no timing started
+    assert lib.minf_timing_read(None, 4, ctypes.byref(cnt)) == M.MINF_EINVAL   # null output array
+    assert lib.minf_timing_read(None, 0, None) == M.MINF_EINVAL
