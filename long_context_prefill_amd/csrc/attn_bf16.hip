@@ -131,16 +131,19 @@ __device__ __forceinline__ ItemLists item_lists(const AttnParams& P, size_t bh, 
 // queue per XCD: the attention kernel runs persistent work-groups (four per
 // CU) and work-group i serves the queue of XCD i mod 8, the XCD the
 // hardware dispatches it to.  Items are grouped into units:
-// * a Vertical-Slash or A-shape unit is one (batch, head) pair, or a
-//   contiguous range of its query blocks when there are fewer than 32 pairs;
-//   its blocks are queued from the last to the first;
+// * a Vertical-Slash or A-shape unit is a run of consecutive query blocks of
+//   one (batch, head) pair (the run length comes from attn_sched_shape); its
+//   blocks are queued from the last to the first;
 // * a Block-Sparse unit holds every Block-Sparse head of one (batch, KV
-//   group) over such a block range, interleaved per query block: heads that
-//   share K and V and select nearly the same key blocks run side by side.
-// Units are costed by their exact chunk counts and assigned largest first to
-// the least-loaded XCD.  The work-groups that run together on one XCD are
-// then consecutive query blocks of one head (or one KV group), whose key sets
-// largely coincide, so their K/V rows are shared in that XCD's L2.
+//   group) over such a run, interleaved per query block: heads that share K
+//   and V and select nearly the same key blocks run side by side.
+// Units are costed by their exact chunk counts.  KV groups are taken in
+// order, and within a group the units are assigned largest first to the
+// least-loaded XCD, so the eight XCDs work through the groups together and
+// the active group's K and V stay in the memory-side cache.  The
+// work-groups that run together on one XCD are consecutive query blocks of
+// one head (or one KV group), whose key sets largely coincide, so their K/V
+// rows are also shared in that XCD's L2.
 
 // Block-Sparse heads of h's KV group: their number, and h's rank among them.
 __device__ __forceinline__ int bs_group(const AttnParams& P, int h, int* rank) {
@@ -204,11 +207,15 @@ __global__ __launch_bounds__(256) void attn_cost_kernel(AttnParams P) {
 
 __global__ __launch_bounds__(256) void attn_sched_kernel(AttnParams P) {
   const int U = P.sched_units;
-  // rank by (cost descending, unit ascending)
+  // The units of one KV group are contiguous (heads g0 .. g0 + gsz - 1 of one
+  // batch entry); rank them by (group ascending, cost descending, unit
+  // ascending), comparing within the group only.
+  const int per_group = P.gsz * P.sched_P;
   for (int u = threadIdx.x; u < U; u += 256) {
     const long long cu = P.sched_cost[u];
-    int r = 0;
-    for (int v = 0; v < U; ++v) {
+    const int g0 = u - u % per_group;
+    int r = g0;
+    for (int v = g0; v < g0 + per_group; ++v) {
       const long long cv = P.sched_cost[v];
       r += (cv > cu) || (cv == cu && v < u);
     }

@@ -145,7 +145,7 @@ struct AttnWs { size_t cost, order, uxcd, uoff, queue, meta, total; int P, R, un
 AttnWs attn_ws(const minf_problem* p, const Derived& d) {
   Carve c;
   AttnWs w;
-  minf::attn_sched_shape(p->B, p->Hq, d.nq, &w.P, &w.R);
+  minf::attn_sched_shape(p->B, p->Hq, p->Hkv, d.nq, &w.P, &w.R);
   w.units = p->B * p->Hq * w.P;
   w.cost = c.take((size_t)w.units * 8);
   w.order = c.take((size_t)w.units * 4);

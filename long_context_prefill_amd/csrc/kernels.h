@@ -37,12 +37,25 @@ struct AttnParams {
   int32_t sched_P, sched_R, sched_units;
 };
 // Units of the attention schedule for B*Hq heads and nq query blocks.
-inline void attn_sched_shape(int B, int Hq, int64_t nq, int* P, int* R) {
+// Units of the bf16 attention schedule: each head's query blocks are cut
+// into P runs of R consecutive blocks.  About kUnitsPerGroup units per KV
+// group, so that one group's work spreads evenly over the eight XCD queues
+// and every XCD works on the same group at about the same time (that group's
+// K and V then stay in the memory-side cache); but runs of at least
+// kMinRun blocks, so that the work-groups running together on one XCD
+// (4 per CU, 32 CUs) mostly work on neighbouring blocks of one head; and at
+// most kMaxUnits units in all.
+constexpr int kUnitsPerGroup = 32;
+constexpr int kMinRun = 128;
+constexpr int kMaxUnits = 4096;
+inline void attn_sched_shape(int B, int Hq, int Hkv, int64_t nq, int* P, int* R) {
   const int bh = B * Hq;
-  int parts = bh >= 32 ? 1 : (32 + bh - 1) / bh;
-  if (parts > nq) parts = (int)nq;
+  const int g = Hq / Hkv;
+  int64_t parts = (kUnitsPerGroup + g - 1) / g;
+  if (parts > nq / kMinRun) parts = nq / kMinRun;
+  if (parts * bh > kMaxUnits) parts = kMaxUnits / bh;
   if (parts < 1) parts = 1;
-  *P = parts;
+  *P = (int)parts;
   *R = (int)((nq + parts - 1) / parts);
 }
 hipError_t launch_attn(const AttnParams& p, int in_bf16, int dh, hipStream_t st);
