@@ -46,6 +46,7 @@ namespace minf {
 namespace {
 
 typedef float floatx16 __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x16 __attribute__((ext_vector_type(16)));
 typedef short short4_t __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) short4_t lds_short4;
 typedef __attribute__((address_space(3))) const u32x4 lds_u32x4;
@@ -76,12 +77,16 @@ __device__ __forceinline__ int32_t ld_uniform(const int32_t* p, int64_t i) {
   return ((const __attribute__((address_space(4))) int32_t*)p)[i];
 }
 
+// A chunk of 32 keys as the pipeline sees it (wave-uniform).
+constexpr int kFast = 1;     // keys kstart .. kstart+31, all inside [0, n): one affine copy
+constexpr int kMask = 2;     // some pair of this wave's rows needs the per-element test
+constexpr int kNone = 4;     // no pair of this wave's rows is kept
+constexpr int kGather = 8;   // keys are column-list entries kstart .. kstart+vhi-1
+constexpr int kWin = 16;     // an A-shape window chunk: keys j >= i - window + 1 only
 struct Chunk {
-  int kstart;         // first key of a contiguous chunk
-  int vlo, vhi;       // keys kept from a contiguous chunk
-  int win;            // > 0: also j >= i - win + 1
-  const int32_t* gp;  // key list of a gathered chunk, else nullptr
-  int gcnt;           // entries of gp
+  int kstart;   // first key (contiguous) or first column-list entry (gathered)
+  int vlo, vhi; // contiguous: keys kept within the chunk; gathered: vhi = entries
+  int flags;
 };
 
 // The chunk lists of one work item (batch/head bh, query block u): Ca chunks
@@ -383,29 +388,56 @@ __device__ __forceinline__ void attn_item(const AttnParams& P, const int b, cons
   const int whi = __builtin_amdgcn_readfirstlane(L.whi);
   const int win = __builtin_amdgcn_readfirstlane(L.win);
   const int ncols = __builtin_amdgcn_readfirstlane(L.ncols);
+  const int rlast = rw0 + 31;     // this wave's last row
 
-  auto describe = [&](int k, Chunk& d) {
-    d.gp = nullptr; d.gcnt = 0; d.win = 0;
+  // Flags of a contiguous chunk whose keys kstart .. kstart+31 are kept
+  // within [vlo, vhi], besides the causal limit and, for a window chunk
+  // (w), the window limit of each row.  kNone may be conservative (unset
+  // although nothing is kept); the per-element test is then exact.
+  auto cflags = [&](int kstart, int vlo, int vhi, bool w) {
+    int f = (kstart >= 0 && kstart + 31 < n) ? kFast : 0;
+    const int lo = w ? max(vlo, rw0 - win + 1) : vlo;
+    if (lo > min(vhi, rlast)) return f | kNone;
+    if (vlo > kstart || vhi < kstart + 31 || kstart + 31 > rw0 || (w && kstart < rlast - win + 1)) f |= kMask;
+    return f;
+  };
+  // Chunk k of this item (wave-uniform).
+  auto describe = [&](int k) {
+    Chunk d;
     if constexpr (KIND == MINF_ASHAPE) {
-      if (k < Ca) {
-        d.kstart = 32 * k; d.vlo = d.kstart; d.vhi = min(d.kstart + 31, sink_len - 1);
-      } else {
-        d.kstart = wlo + 32 * (k - Ca); d.vlo = d.kstart; d.vhi = min(d.kstart + 31, whi); d.win = win;
-      }
+      const bool w = k >= Ca;
+      d.kstart = w ? wlo + 32 * (k - Ca) : 32 * k;
+      d.vlo = d.kstart;
+      d.vhi = min(d.kstart + 31, w ? whi : sink_len - 1);
+      d.flags = cflags(d.kstart, d.vlo, d.vhi, w) | (w ? kWin : 0);
     } else if constexpr (KIND == MINF_VSLASH) {
       if (k < Ca) {
         const int lo = ld_uniform(L.clo, k), hi = ld_uniform(L.chi, k);
-        d.kstart = row0 - hi; d.vlo = max(0, d.kstart); d.vhi = min(row0 - lo, n - 1);
+        d.kstart = row0 - hi;
+        d.vlo = max(0, d.kstart);
+        d.vhi = min(row0 - lo, n - 1);
+        d.flags = cflags(d.kstart, d.vlo, d.vhi, false);
       } else {
-        const int kk = k - Ca;
-        d.gp = L.colrow + 32 * kk; d.gcnt = min(32, ncols - 32 * kk);
-        d.kstart = 0; d.vlo = 0; d.vhi = n - 1;
+        const int e = 32 * (k - Ca);
+        const int cnt = min(32, ncols - e);
+        const int gfirst = ld_uniform(L.colrow, e), glast = ld_uniform(L.colrow, e + cnt - 1);
+        d.kstart = e;
+        d.vlo = 0;
+        d.vhi = cnt;
+        d.flags = kGather | (gfirst > rlast ? kNone : 0) | ((cnt < 32 || glast > rw0) ? kMask : 0);
       }
     } else {
       const int vb = ld_uniform(L.blkrow, k >> 1);
-      d.kstart = 64 * vb + 32 * (k & 1); d.vlo = d.kstart; d.vhi = min(d.kstart + 31, n - 1);
-      if (vb < 0 || vb > u) { d.kstart = 0; d.vlo = 1; d.vhi = 0; }   // not a causal block: keep nothing
+      if (vb < 0 || vb > u) {   // not a causal block: keep nothing
+        d.kstart = 0; d.vlo = 1; d.vhi = 0; d.flags = kNone;
+      } else {
+        d.kstart = 64 * vb + 32 * (k & 1);
+        d.vlo = d.kstart;
+        d.vhi = min(d.kstart + 31, n - 1);
+        d.flags = cflags(d.kstart, d.vlo, d.vhi, false);
+      }
     }
+    return d;
   };
 
   // ---- copy offsets.  Wave w copies rows 16w + 4i + lane/16 (i = 0..3) of
@@ -426,7 +458,7 @@ __device__ __forceinline__ void attn_item(const AttnParams& P, const int b, cons
   auto issue = [&](const Chunk& d, int sl, bool is_v) {
     const char* src = is_v ? Vb : Kb;
     const uint32_t dst = __builtin_amdgcn_readfirstlane(lds_base + sl * kSlotB + (is_v ? kTileB : 0));
-    if (!d.gp && d.kstart >= 0 && d.kstart + 31 < n) {
+    if (d.flags & kFast) {
       copy_chunk(src + (size_t)d.kstart * kRowB, is_v ? voff : koff, dst);
     } else {
       // per-lane rows: clamped into [0, n) (the excess keys are masked) or
@@ -436,7 +468,7 @@ __device__ __forceinline__ void attn_item(const AttnParams& P, const int b, cons
       for (int i = 0; i < 4; ++i) {
         const int r = crow0 + 4 * i;
         int key = d.kstart + r;
-        if (d.gp) key = r < d.gcnt ? d.gp[r] : 0;
+        if (d.flags & kGather) key = r < d.vhi ? L.colrow[d.kstart + r] : 0;
         const uint32_t rb = (uint32_t)min(max(key, 0), n - 1) * kRowB;
         o[i] = rb + 16 * (cpiece ^ (is_v ? 4 * (r & 3) : (r & 15)));
       }
@@ -444,6 +476,48 @@ __device__ __forceinline__ void attn_item(const AttnParams& P, const int b, cons
     }
   };
 
+  // Keep-bits of a chunk for this lane's row: bit 8a + b (a, b = 0..3) set
+  // when the key at chunk position 8a + 4hh + b, which element 4a + b of
+  // the lane holds, is kept.  Only for chunks with kMask; gathered chunks
+  // read their keys with vector loads, so this runs while no copy is in
+  // flight.
+  auto keep_bits = [&](const Chunk& d) -> uint32_t {
+    if (!(d.flags & kMask) || (d.flags & kNone)) return 0u;
+    if (d.flags & kGather) {
+      uint32_t bits = 0;
+      #pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int pos = 8 * (i >> 2) + 4 * hh + (i & 3);
+        const int key = pos < d.vhi ? L.colrow[d.kstart + pos] : n;
+        bits |= (key <= myrow ? 1u : 0u) << (8 * (i >> 2) + (i & 3));
+      }
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      return bits;
+    }
+    const int lo = ((d.flags & kWin) ? max(d.vlo, myrow - win + 1) : d.vlo) - d.kstart;
+    const int hi = min(d.vhi, myrow) - d.kstart;
+    const int a = max(lo, 0), z = min(hi, 31);
+    const uint32_t m = a > z ? 0u : ((0xffffffffu >> (31 - z)) & (0xffffffffu << a));
+    return m >> (4 * hh);
+  };
+  // exclusion (section 5.1): pairs outside the candidate set are -inf before
+  // the maximum
+  auto apply_mask = [&](floatx16& s, const Chunk& d, uint32_t bits) {
+    if (d.flags & kNone) {
+      #pragma unroll
+      for (int i = 0; i < 16; ++i) s[i] = kNegInf;
+    } else if (d.flags & kMask) {
+      // (the vector is reinterpreted whole: bit-casting single elements of a
+      // vector has been miscompiled into reads of element 0)
+      u32x16 v = __builtin_bit_cast(u32x16, s);
+      #pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const uint32_t keep = (uint32_t)__builtin_amdgcn_sbfe((int)bits, 8 * (i >> 2) + (i & 3), 1);
+        v[i] = (v[i] & keep) | (0xff800000u & ~keep);
+      }
+      s = __builtin_bit_cast(floatx16, v);
+    }
+  };
   // ---- operand read offsets within a slot
   // K: lane l reads row l%32, piece 2t + hh
   // V^T (transposing read): lane 16G + 4r + qq supplies row 16s + 8rho + 4(G/2) + r,
@@ -471,60 +545,6 @@ __device__ __forceinline__ void attn_item(const AttnParams& P, const int b, cons
   typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
   const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
 
-  // What a chunk needs from this wave (wave-uniform): whether any of its keys
-  // survives for the wave's rows, and whether some pair needs the per-element
-  // test.  For a gathered chunk that needs the test, gbits gets bit i set when
-  // the lane's i-th key (position 8(i/4) + 4hh + i%4) is kept for its row.
-  // Called while no copy is in flight (its vector loads are waited for).
-  struct Plan { bool any, mask; uint32_t gbits; };
-  auto plan = [&](const Chunk& d) {
-    Plan pl{false, false, 0u};
-    if (d.gp) {
-      if (d.gcnt <= 0) return pl;
-      const int gfirst = ld_uniform(d.gp, 0);
-      const int glast = ld_uniform(d.gp, d.gcnt - 1);
-      pl.any = gfirst <= rw0 + 31;
-      pl.mask = d.gcnt < 32 || glast > rw0;
-      if (pl.any && pl.mask) {
-        #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int pos = 8 * (i >> 2) + 4 * hh + (i & 3);
-          const int key = pos < d.gcnt ? d.gp[pos] : n;
-          pl.gbits |= (key <= myrow ? 1u : 0u) << i;
-        }
-        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-      }
-    } else {
-      const int hi = min(d.vhi, rw0 + 31);
-      const int lo = d.win > 0 ? max(d.vlo, rw0 - d.win + 1) : d.vlo;
-      pl.any = lo <= hi;
-      pl.mask = d.kstart < d.vlo || d.kstart + 31 > d.vhi || d.kstart + 31 > rw0 ||
-                (d.win > 0 && d.kstart < rw0 + 31 - d.win + 1);
-    }
-    return pl;
-  };
-  // exclusion (section 5.1): pairs outside the candidate set are -inf before
-  // the maximum; element i holds key position 8(i/4) + 4hh + i%4 of the chunk
-  auto apply_mask = [&](floatx16& s, const Chunk& d, const Plan& pl) {
-    if (!pl.any) {
-      #pragma unroll
-      for (int i = 0; i < 16; ++i) s[i] = kNegInf;
-    } else if (pl.mask) {
-      if (d.gp) {
-        #pragma unroll
-        for (int i = 0; i < 16; ++i)
-          if (!((pl.gbits >> i) & 1u)) s[i] = kNegInf;
-      } else {
-        const int hi = min(d.vhi, myrow) - d.kstart;
-        const int lo = (d.win > 0 ? max(d.vlo, myrow - d.win + 1) : d.vlo) - d.kstart;
-        #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int pos = 8 * (i >> 2) + 4 * hh + (i & 3);
-          if (!(pos >= lo && pos <= hi)) s[i] = kNegInf;
-        }
-      }
-    }
-  };
   auto read_k = [&](int sl, u32x4 (&kop)[8]) {
     const uint32_t base = sbase + sl * kSlotB;
     #pragma unroll
@@ -575,17 +595,16 @@ __device__ __forceinline__ void attn_item(const AttnParams& P, const int b, cons
   //      copies issued in iteration j are V of chunk j+1 and K of chunk j+2, so
   //      every slot half is rewritten only after both waves have passed the
   //      barrier that ends its last use.
-  Chunk d0, d1, d2;
-  describe(kc, d0);
+  Chunk d0 = describe(kc), d1{0, 1, 0, kNone}, d2{0, 1, 0, kNone};
   issue(d0, 0, false);
   issue(d0, 0, true);
   if (C > 1) {
     advance();
-    describe(kc, d1);
+    d1 = describe(kc);
     issue(d1, 1, false);
   }
   wait_copies_and_barrier();
-  Plan p0 = plan(d0);
+  uint32_t bits0 = keep_bits(d0);
   floatx16 s_cur;
   {
     u32x4 kop[8];
@@ -600,15 +619,15 @@ __device__ __forceinline__ void attn_item(const AttnParams& P, const int b, cons
     u32x4 kop[8], vop[2][4];
     const bool more = j + 1 < C;
     read_k(sl ^ 1, kop);
-    Plan p1{false, false, 0u};
-    if (more) p1 = plan(d1);
+    uint32_t bits1 = 0u;
+    if (more) bits1 = keep_bits(d1);
     if (more) issue(d1, sl ^ 1, true);
     if (j + 2 < C) {
       advance();
-      describe(kc, d2);
+      d2 = describe(kc);
       issue(d2, sl, false);
     }
-    apply_mask(s_cur, d0, p0);
+    apply_mask(s_cur, d0, bits0);
 
     // online softmax of chunk j with lazy rescaling
     float mx = fmaxf(fmaxf(fmaxf(s_cur[0], s_cur[1]), fmaxf(s_cur[2], s_cur[3])),
@@ -658,7 +677,7 @@ __device__ __forceinline__ void attn_item(const AttnParams& P, const int b, cons
     s_cur = s_next;
     d0 = d1;
     d1 = d2;
-    p0 = p1;
+    bits0 = bits1;
   };
 
   for (int j = 0; j < C; j += 2) {
