@@ -171,6 +171,83 @@ def cpu_baseline(p, workers):
                       f"all heads and all {p.n} rows"}
 
 
+def dense_heads(Hq, n):
+    """The dense causal baseline on the same kernels: every head A-shape with
+    no sink and a window of n keys, i.e. all j <= i."""
+    from synth import gen
+    return [gen.ashape(0, n)] * Hq
+
+
+def time_layer(M, prob, heads, Q, K, V, O_, steps, warmup, index=True, flush=None):
+    """Median event-timed ms of (index stages,) tile build and attention."""
+    import numpy as np
+    import torch
+    buf = M.alloc_buffers(prob, heads)
+    t = buf["tiles"]
+    stream = torch.cuda.current_stream()
+
+    def step():
+        if index:
+            M.minf_vs_index(prob, heads, Q, K, buf["vert_idx"], buf["slash_idx"], None, None, buf["ws"])
+            M.minf_bs_index(prob, heads, Q, K, buf["blk_idx"], buf["blk_cnt"], buf["ws"])
+        M.minf_build_tiles(prob, heads, buf["vert_idx"], buf["slash_idx"], buf["blk_idx"], buf["blk_cnt"], t,
+                           buf["ws"])
+        M.minf_sparse_attn(prob, heads, Q, K, V, buf["blk_idx"], buf["blk_cnt"], t, O_, None, buf["ws"])
+
+    for _ in range(warmup):
+        step()
+    ms = []
+    for _ in range(steps):
+        if flush is not None:
+            flush.fill_(1.0)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        step()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        ms.append(e0.elapsed_time(e1))
+    if int(t["status"].item()) != 0:
+        raise RuntimeError(f"device status {int(t['status'].item())}")
+    kept = int(t["kept_edges"].sum().item())
+    del buf
+    return float(np.median(ms)), kept
+
+
+def crossover(a):
+    """Sparse layer (index + attention, the 128K mixed pattern table) against
+    the dense causal baseline over sequence lengths, on planted inputs of
+    each length; one JSON line."""
+    import numpy as np
+    import torch
+    import long_context_prefill_amd as M
+    from synth import gen
+    flush = torch.empty(1 << 28, dtype=torch.float32, device="cuda")
+    rows = []
+    for n in [int(x) for x in a.crossover.split(",")]:
+        t0 = time.time()
+        p = gen.generate(f"crossover_n{n}", 1, 32, 8, n, 128, "bf16", gen.pattern_table(3), 1003,
+                         dist="planted", sample_rows=4096)
+        log(f"generated n={n} in {time.time() - t0:.1f}s")
+        conv = lambda x: torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).cuda()
+        Q, K, V = conv(p.Q), conv(p.K), conv(p.V)
+        O_ = torch.empty((1, 32, n, 128), dtype=torch.float32, device="cuda")
+        prob = M.make_problem(1, 32, 8, n, 128, "bf16", "f32", 0.0)
+        ms_s, kept_s = time_layer(M, prob, M.make_heads(p.heads), Q, K, V, O_, a.steps, a.warmup, True, flush)
+        ms_d, kept_d = time_layer(M, prob, M.make_heads(dense_heads(32, n)), Q, K, V, O_, a.steps, a.warmup,
+                                  False, flush)
+        rows.append({"n": n, "sparse_ms": round(ms_s, 3), "dense_ms": round(ms_d, 3),
+                     "speedup": round(ms_d / ms_s, 3), "sparse_kept_edges": kept_s, "dense_edges": kept_d,
+                     "dense_tflops": round(4 * 128 * kept_d / (ms_d * 1e-3) / 1e12, 1)})
+        log(json.dumps(rows[-1]))
+        del Q, K, V, O_
+    wins = [r["n"] for r in rows if r["speedup"] > 1.0]
+    print(json.dumps({"metric": "sparse vs dense causal prefill ms/layer by sequence length",
+                      "unit": "ms/layer", "higher_is_better": False, "n_gpus": 1, "dtype": "bf16",
+                      "config": {"workload": "planted B=1 Hq=32 Hkv=8 dh=128, 128K mixed pattern table",
+                                 "lengths": [r["n"] for r in rows]},
+                      "rows": rows, "sparse_wins_from_n": min(wins) if wins else None}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -181,6 +258,9 @@ def main():
     ap.add_argument("--no-flush", action="store_true",
                     help="skip the 1 GiB cache-flushing write before each timed step")
     ap.add_argument("--out-dtype", default="f32", choices=["f32", "bf16"])
+    ap.add_argument("--crossover", default="",
+                    help="comma-separated lengths: time the sparse layer against the dense causal baseline")
+    ap.add_argument("--no-dense", action="store_true", help="skip the dense causal baseline")
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="only run a plain device copy of this many MiB (memory-counter calibration)")
     a = ap.parse_args()
@@ -191,6 +271,9 @@ def main():
 
     if a.copy_mib:
         copy_probe(a.copy_mib, max(1, a.steps))
+        return
+    if a.crossover:
+        crossover(a)
         return
 
     import numpy as np
@@ -283,6 +366,17 @@ def main():
     dense = p.B * p.Hq * p.n * (p.n + 1) // 2
     computed = computed_pairs(p, t, buf)
 
+    dense = None
+    if not a.no_dense:
+        t0 = time.time()
+        ms_d, kept_d = time_layer(M, prob, M.make_heads(dense_heads(p.Hq, p.n)), Q, K, V, O_, 3, 1, False, flush)
+        dense = {"ms": round(ms_d, 3), "kept_edges": kept_d,
+                 "tflops": round(4 * p.dh * kept_d / (ms_d * 1e-3) / 1e12, 1),
+                 "speedup_of_sparse": round(ms_d / ms_step, 3),
+                 "what": "same inputs, every head A-shape(sink 0, window n) = all j <= i; tile build + attention, "
+                         "median of 3 cache-flushed steps"}
+        log(f"dense baseline in {time.time() - t0:.1f}s")
+
     cpu = None
     if not a.no_cpu_baseline:
         try:
@@ -333,6 +427,7 @@ def main():
                      "kernel": ATTN_KERNEL if (p.dtype == "bf16" and p.dh == 128) else "attn_kernel",
                      "per_launch_flops": flops, "avg_launch_ms": round(ms_kernel, 4),
                      "launches_timed": len(kern)},
+        "dense_baseline": dense,
         "cpu_baseline": cpu,
         "context": "pages: up to 10x prefill speedup over dense on an A100 (another machine and workload)",
     }

@@ -202,3 +202,34 @@ def test_bad_indices_set_status_and_stay_in_bounds():
     o = O_.cpu().numpy()
     assert np.all(o[0, 0] == 0) and np.all(o[0, 1] == 0) and np.all(o[0, 2] == 0)
     assert np.all(np.isfinite(o[0, 3])) and np.abs(o[0, 3]).max() > 0
+
+
+@pytest.mark.parametrize("n", [1000, 2113])
+def test_dense_causal_baseline_as_full_window(n):
+    """The dense causal baseline runs on the same kernels as an A-shape head
+    with no sink and a window of n keys, i.e. N(i) = {j <= i} ([MInf]
+    section 1.1, Eq. 1-2).  Checked against the textbook dense causal
+    softmax attention of the oracle, and kept edges = n(n+1)/2 per head."""
+    U.log(f"dense n={n}")
+    p = gen.make_small(n=n, Hq=4, Hkv=2, dh=128, seed=21, heads=[gen.ashape(0, n)] * 4)
+    import torch
+    prob = U.make_prob(p)
+    heads = M.make_heads(p.heads)
+    buf = M.alloc_buffers(prob, heads)
+    Q, K, V = U.device_inputs(p)
+    O_ = torch.full((p.B, p.Hq, n, p.dh), float("nan"), dtype=torch.float32, device="cuda")
+    M.minf_build_tiles(prob, heads, buf["vert_idx"], buf["slash_idx"], buf["blk_idx"], buf["blk_cnt"],
+                       buf["tiles"], buf["ws"])
+    M.minf_sparse_attn(prob, heads, Q, K, V, buf["blk_idx"], buf["blk_cnt"], buf["tiles"], O_, None, buf["ws"])
+    torch.cuda.synchronize()
+    ke = buf["tiles"]["kept_edges"].cpu().numpy()
+    assert np.all(ke == n * (n + 1) // 2)
+    Og = O_.cpu().numpy()
+    ref = np.zeros_like(Og, dtype=np.float64)
+    g = p.Hq // p.Hkv
+    for h in range(p.Hq):
+        q = O.widen(p.Q[0, h], p.dtype)
+        k = O.widen(p.K[0, h // g], p.dtype)
+        v = O.widen(p.V[0, h // g], p.dtype)
+        ref[0, h], _ = O.dense_attention(q, k, v, p.eff_scale)
+    U.compare_output(Og, ref, p.dtype, f"dense n={n}")
