@@ -40,6 +40,8 @@
 //   copies write 4 whole rows per instruction.
 // * Occupancy: 4 work-groups (8 waves) per CU, two waves per SIMD, so one
 //   wave's softmax overlaps the other's matrix products.
+#include <type_traits>
+
 #include "kernels.h"
 
 namespace minf {
@@ -614,15 +616,17 @@ __device__ __forceinline__ void attn_item(const AttnParams& P, const int b, cons
   // iteration 0 rewrites the K half of slot 0, which both waves just read
   wait_copies_and_barrier();
 
-  auto iteration = [&](const int j, const int sl) {
+  // STEADY: chunks j+1 and j+2 exist (no bound tests)
+  auto iteration = [&](const int j, const int sl, auto steady) {
+    constexpr bool STEADY = decltype(steady)::value;
     // slot sl holds K and V of chunk j, slot sl^1 holds K of chunk j+1
     u32x4 kop[8], vop[2][4];
-    const bool more = j + 1 < C;
+    const bool more = STEADY || j + 1 < C;
     read_k(sl ^ 1, kop);
     uint32_t bits1 = 0u;
     if (more) bits1 = keep_bits(d1);
     if (more) issue(d1, sl ^ 1, true);
-    if (j + 2 < C) {
+    if (STEADY || j + 2 < C) {
       advance();
       d2 = describe(kc);
       issue(d2, sl, false);
@@ -680,11 +684,18 @@ __device__ __forceinline__ void attn_item(const AttnParams& P, const int b, cons
     bits0 = bits1;
   };
 
-  for (int j = 0; j < C; j += 2) {
-    iteration(j, 0);
+  int j = 0;
+  for (; j + 3 < C; j += 2) {
+    iteration(j, 0, std::true_type{});
+    wait_copies_and_barrier();
+    iteration(j + 1, 1, std::true_type{});
+    wait_copies_and_barrier();
+  }
+  for (; j < C; j += 2) {
+    iteration(j, 0, std::false_type{});
     if (j + 1 >= C) break;
     wait_copies_and_barrier();
-    iteration(j + 1, 1);
+    iteration(j + 1, 1, std::false_type{});
     if (j + 2 >= C) break;
     wait_copies_and_barrier();
   }
