@@ -261,6 +261,7 @@ def main():
     ap.add_argument("--crossover", default="",
                     help="comma-separated lengths: time the sparse layer against the dense causal baseline")
     ap.add_argument("--no-dense", action="store_true", help="skip the dense causal baseline")
+    ap.add_argument("--no-exact", action="store_true", help="skip the exact slash pairs (slash_tile=1) layer")
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="only run a plain device copy of this many MiB (memory-counter calibration)")
     a = ap.parse_args()
@@ -377,6 +378,17 @@ def main():
                          "median of 3 cache-flushed steps"}
         log(f"dense baseline in {time.time() - t0:.1f}s")
 
+    exact = None
+    if not a.no_exact and "vslash" in per_kind:
+        t0 = time.time()
+        prob1 = M.make_problem(p.B, p.Hq, p.Hkv, p.n, p.dh, p.dtype, a.out_dtype, p.scale, slash_tile=1)
+        ms_e, kept_e = time_layer(M, prob1, heads, Q, K, V, O_, 3, 1, True, flush)
+        exact = {"ms": round(ms_e, 3), "kept_edges": kept_e,
+                 "what": "same layer with slash_tile=1 (Eq. 5 pairs: row i keeps key j iff i-j is a selected "
+                         "offset or j a selected column); index + tiles + attention, median of 3 cache-flushed "
+                         "steps"}
+        log(f"exact slash pairs in {time.time() - t0:.1f}s")
+
     cpu = None
     if not a.no_cpu_baseline:
         try:
@@ -428,6 +440,7 @@ def main():
                      "per_launch_flops": flops, "avg_launch_ms": round(ms_kernel, 4),
                      "launches_timed": len(kern)},
         "dense_baseline": dense,
+        "exact_slash_pairs": exact,
         "cpu_baseline": cpu,
         "context": "pages: up to 10x prefill speedup over dense on an A100 (another machine and workload)",
     }

@@ -84,10 +84,13 @@ typedef struct {
 /* Problem shape.  Constraints: B >= 1; 1 <= Hq <= 64; Hkv >= 1 and
  * Hq % Hkv == 0; n >= 1; dh in {64, 128}; in_dtype F32 or BF16 (Q, K and V
  * share it); out_dtype F32 or BF16; scale > 0 or 0 for 1/sqrt(dh);
- * block == 64; slash_tile == 64 (each slash offset d covers, for query
- * block u, the keys [64u - d, 64u + 63 - d]: the 64x64 physical tile of
- * section 2.1 of the MInference page).  slash_tile == 1 (the logical pairs
- * of Eq. 5) is answered with MINF_EUNSUPPORTED. */
+ * block == 64; slash_tile == 64 or 1.  slash_tile == 64: each slash offset
+ * d covers, for query block u, the keys [64u - d, 64u + 63 - d] (the 64x64
+ * physical tile of section 2.1 of the MInference page).  slash_tile == 1:
+ * the logical pairs of Eq. 5, i.e. key j is kept for row i iff i - j is a
+ * selected offset or j a selected column (and j <= i); the tile lists are
+ * the same, and the attention tests each pair against two per-head bitmaps
+ * that minf_build_tiles writes (minf_tiles.slash_bits / col_bits). */
 typedef struct {
   int32_t B, Hq, Hkv, n, dh;
   int32_t in_dtype;
@@ -105,6 +108,8 @@ typedef struct {
   int64_t max_kb;      /* key blocks per BS query block: max of min(k_b, nq)         */
   int64_t max_chunks;  /* slash-span chunks per VS head                              */
   int64_t ws_bytes;    /* workspace bytes that suffice for every call below          */
+  int64_t bits_words;  /* 32-bit words of each per-head bitmap of minf_tiles when
+                          slash_tile == 1 and the layer has a VS head, else 0      */
 } minf_sizes;
 
 /* Tile lists produced by minf_build_tiles and read by minf_sparse_attn.
@@ -128,9 +133,15 @@ typedef struct {
  *                     column list so no pair is counted twice).
  *   col_cnt           [B, Hq, nq]
  *   kept_edges        [B, Hq] int64       E_h = sum_i |N_h(i)|, exact, for every
- *                     head (A-shape in closed form).
+ *                     head (A-shape in closed form), under the problem's
+ *                     slash_tile.
  *   status            [1]                 OR of MINF_DEV_* bits; the caller
- *                     zeroes it before the first call. */
+ *                     zeroes it before the first call.
+ *   slash_bits, col_bits [B, Hq, bits_words] uint32, only for slash_tile == 1
+ *                     (else may be NULL): bit n + 127 - d of slash_bits is set
+ *                     iff d is a selected offset, bit j + 128 of col_bits iff
+ *                     j is a selected column (bit b is bit b%32 of word b/32;
+ *                     the other bits are zero). */
 typedef struct {
   int32_t* span_lo;
   int32_t* span_hi;
@@ -142,6 +153,8 @@ typedef struct {
   int32_t* col_cnt;
   int64_t* kept_edges;
   int32_t* status;
+  uint32_t* slash_bits;
+  uint32_t* col_bits;
 } minf_tiles;
 
 enum {

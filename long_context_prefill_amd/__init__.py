@@ -54,13 +54,14 @@ class MinfHeadCfg(ctypes.Structure):
 
 class MinfSizes(ctypes.Structure):
     _fields_ = [("nq", ctypes.c_int64), ("max_v", ctypes.c_int64), ("max_s", ctypes.c_int64),
-                ("max_kb", ctypes.c_int64), ("max_chunks", ctypes.c_int64), ("ws_bytes", ctypes.c_int64)]
+                ("max_kb", ctypes.c_int64), ("max_chunks", ctypes.c_int64), ("ws_bytes", ctypes.c_int64),
+                ("bits_words", ctypes.c_int64)]
 
 
 class MinfTiles(ctypes.Structure):
     _fields_ = [(name, ctypes.c_void_p) for name in
                 ("span_lo", "span_hi", "span_cnt", "chunk_lo", "chunk_hi", "chunk_cnt",
-                 "cols", "col_cnt", "kept_edges", "status")]
+                 "cols", "col_cnt", "kept_edges", "status", "slash_bits", "col_bits")]
 
 
 _lib = None
@@ -231,6 +232,9 @@ def alloc_buffers(prob: MinfProblem, heads, device="cuda"):
             "status": torch.zeros(1, **i32),
         },
     }
+    if int(sz.bits_words) > 0:
+        buf["tiles"]["slash_bits"] = torch.zeros((B, Hq, int(sz.bits_words)), **i32)
+        buf["tiles"]["col_bits"] = torch.zeros((B, Hq, int(sz.bits_words)), **i32)
     return buf
 
 

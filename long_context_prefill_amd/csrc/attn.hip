@@ -53,6 +53,7 @@ struct ChunkDesc {
   int gcnt;              // valid entries of gp
   int win;               // > 0: window lower bound j >= i - win + 1 applies
   bool mask;             // per-element test needed
+  bool exact;            // a slash span chunk under exact pairs (slash_tile == 1)
 };
 
 template <typename T, int DH>
@@ -245,7 +246,7 @@ __global__ __launch_bounds__(256, 1) void attn_kernel(AttnParams P) {
 
   // ---- chunk description (wave-uniform)
   auto describe = [&](int k, ChunkDesc& d) {
-    d.gp = nullptr; d.gcnt = 0; d.win = 0;
+    d.gp = nullptr; d.gcnt = 0; d.win = 0; d.exact = false;
     if (kind == MINF_ASHAPE) {
       if (k < Ca) {
         d.kstart = 32 * k; d.vlo = 0; d.vhi = sink_len - 1;
@@ -256,6 +257,7 @@ __global__ __launch_bounds__(256, 1) void attn_kernel(AttnParams P) {
       if (k < Ca) {
         const int lo = clo[k], hi = chi[k];
         d.kstart = row0 - hi; d.vlo = max(0, d.kstart); d.vhi = min(row0 - lo, n - 1);
+        d.exact = P.slash_tile == 1;
       } else {
         const int kk = k - Ca;
         d.gp = colrow + 32 * kk; d.gcnt = min(32, ncols - 32 * kk);
@@ -274,7 +276,7 @@ __global__ __launch_bounds__(256, 1) void attn_kernel(AttnParams P) {
       d.vlo = max(d.vlo, d.kstart);
       d.vhi = min(d.vhi, d.kstart + 31);
       d.mask = (d.kstart < d.vlo) || (d.kstart + 31 > d.vhi) || (d.kstart + 31 > row0) ||
-               (d.win > 0 && d.kstart < row0 + 63 - d.win + 1);
+               (d.win > 0 && d.kstart < row0 + 63 - d.win + 1) || d.exact;
     }
   };
   // The lane's K-operand rows (positions 16*half + r16) are loaded into k;
@@ -328,7 +330,17 @@ __global__ __launch_bounds__(256, 1) void attn_kernel(AttnParams P) {
       #pragma unroll
       for (int e = 0; e < 8; ++e) {
         const int o = ko[e];
-        if (!(o >= lo && o <= hi)) s[e >> 2][nb][e & 3] = kNegInf;
+        bool keep = o >= lo && o <= hi;
+        if (keep && d.exact) {
+          // Eq. 5 taken literally: row - key a selected offset, or key a
+          // selected column (bitmaps from the tile stage)
+          const int key = kb0 + o;
+          const int bs = n + kBitsPad - 1 - (row - key), bc = key + kBitsPad;
+          const uint32_t* sw = P.slash_bits + bh * P.bits_words;
+          const uint32_t* cw = P.col_bits + bh * P.bits_words;
+          keep = ((sw[bs >> 5] >> (bs & 31)) & 1u) || ((cw[bc >> 5] >> (bc & 31)) & 1u);
+        }
+        if (!keep) s[e >> 2][nb][e & 3] = kNegInf;
       }
     }
   };

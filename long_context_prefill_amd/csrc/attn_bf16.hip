@@ -85,6 +85,7 @@ constexpr int kMask = 2;     // some pair of this wave's rows needs the per-elem
 constexpr int kNone = 4;     // no pair of this wave's rows is kept
 constexpr int kGather = 8;   // keys are column-list entries kstart .. kstart+vhi-1
 constexpr int kWin = 16;     // an A-shape window chunk: keys j >= i - window + 1 only
+constexpr int kExact = 32;   // a slash span chunk under exact pairs (slash_tile == 1)
 struct Chunk {
   int kstart;   // first key (contiguous) or first column-list entry (gathered)
   int vlo, vhi; // contiguous: keys kept within the chunk; gathered: vhi = entries
@@ -391,6 +392,7 @@ __device__ __forceinline__ void attn_item(const AttnParams& P, const int b, cons
   const int win = __builtin_amdgcn_readfirstlane(L.win);
   const int ncols = __builtin_amdgcn_readfirstlane(L.ncols);
   const int rlast = rw0 + 31;     // this wave's last row
+  const bool exact = KIND == MINF_VSLASH && P.slash_tile == 1;
 
   // Flags of a contiguous chunk whose keys kstart .. kstart+31 are kept
   // within [vlo, vhi], besides the causal limit and, for a window chunk
@@ -419,6 +421,7 @@ __device__ __forceinline__ void attn_item(const AttnParams& P, const int b, cons
         d.vlo = max(0, d.kstart);
         d.vhi = min(row0 - lo, n - 1);
         d.flags = cflags(d.kstart, d.vlo, d.vhi, false);
+        if (exact && !(d.flags & kNone)) d.flags |= kMask | kExact;
       } else {
         const int e = 32 * (k - Ca);
         const int cnt = min(32, ncols - e);
@@ -499,7 +502,26 @@ __device__ __forceinline__ void attn_item(const AttnParams& P, const int b, cons
     const int lo = ((d.flags & kWin) ? max(d.vlo, myrow - win + 1) : d.vlo) - d.kstart;
     const int hi = min(d.vhi, myrow) - d.kstart;
     const int a = max(lo, 0), z = min(hi, 31);
-    const uint32_t m = a > z ? 0u : ((0xffffffffu >> (31 - z)) & (0xffffffffu << a));
+    uint32_t m = a > z ? 0u : ((0xffffffffu >> (31 - z)) & (0xffffffffu << a));
+    if (d.flags & kExact) {
+      // Eq. 5 taken literally: the pair (myrow, kstart + p) is kept iff
+      // myrow - kstart - p is a selected offset or kstart + p a selected
+      // column.  Offset bits: bit n + kBitsPad - 1 - myrow + kstart + p of
+      // slash_bits, a 32-bit window of three words the wave reads together;
+      // column bits: bit kstart + p + kBitsPad of col_bits.
+      const uint32_t* sw = P.slash_bits + bh * P.bits_words;
+      const uint32_t* cw = P.col_bits + bh * P.bits_words;
+      const int w0 = (n + kBitsPad - 1 - rlast + d.kstart) >> 5;
+      const uint32_t W0 = (uint32_t)ld_uniform((const int32_t*)sw, w0);
+      const uint32_t W1 = (uint32_t)ld_uniform((const int32_t*)sw, w0 + 1);
+      const uint32_t W2 = (uint32_t)ld_uniform((const int32_t*)sw, w0 + 2);
+      const int sh = n + kBitsPad - 1 - myrow + d.kstart - 32 * w0;   // 0 .. 62
+      const uint32_t dwin = sh < 32 ? __builtin_amdgcn_alignbit(W1, W0, sh) : __builtin_amdgcn_alignbit(W2, W1, sh - 32);
+      const int cb = d.kstart + kBitsPad;
+      const uint32_t C0 = (uint32_t)ld_uniform((const int32_t*)cw, cb >> 5);
+      const uint32_t C1 = (uint32_t)ld_uniform((const int32_t*)cw, (cb >> 5) + 1);
+      m &= dwin | __builtin_amdgcn_alignbit(C1, C0, cb & 31);
+    }
     return m >> (4 * hh);
   };
   // exclusion (section 5.1): pairs outside the candidate set are -inf before

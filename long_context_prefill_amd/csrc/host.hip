@@ -27,7 +27,7 @@ minf_status fail(minf_status s, const char* fmt, ...) {
 int64_t round_up(int64_t x, int64_t m) { return (x + m - 1) / m * m; }
 
 struct Derived {
-  int64_t nq = 0, max_v = 0, max_s = 0, max_kb = 0, max_chunks = 0, bm_words = 0;
+  int64_t nq = 0, max_v = 0, max_s = 0, max_kb = 0, max_chunks = 0, bm_words = 0, bits_words = 0;
   bool has_a = false, has_vs = false, has_bs = false;
   int hq_vs = 0, hq_bs = 0;
   minf::HeadTable ht{};
@@ -45,8 +45,8 @@ minf_status validate(const minf_problem* p, const minf_head_cfg* heads, Derived*
   if (p->out_dtype != MINF_F32 && p->out_dtype != MINF_BF16) return fail(MINF_EINVAL, "bad out_dtype %d", p->out_dtype);
   if (!(p->scale >= 0.f) || isinf(p->scale)) return fail(MINF_EINVAL, "scale must be finite and >= 0");
   if (p->block != MINF_BLOCK) return fail(MINF_EUNSUPPORTED, "block must be %d (block=%d)", MINF_BLOCK, p->block);
-  if (p->slash_tile == 1) return fail(MINF_EUNSUPPORTED, "slash_tile=1 (logical Eq. 5 slashes) is not implemented on the GPU");
-  if (p->slash_tile != 64) return fail(MINF_EINVAL, "slash_tile must be 64 (slash_tile=%d)", p->slash_tile);
+  if (p->slash_tile != 64 && p->slash_tile != 1)
+    return fail(MINF_EINVAL, "slash_tile must be 64 or 1 (slash_tile=%d)", p->slash_tile);
   if ((int64_t)p->B * p->Hq * p->n * p->dh > ((int64_t)1 << 40)) return fail(MINF_EINVAL, "problem too large");
   d->nq = (p->n + MINF_BLOCK - 1) / MINF_BLOCK;
   d->scale = p->scale > 0.f ? p->scale : 1.0f / sqrtf((float)p->dh);
@@ -97,6 +97,7 @@ minf_status validate(const minf_problem* p, const minf_head_cfg* heads, Derived*
   d->max_kb = std::max<int64_t>(mk, 1);
   d->max_chunks = (p->n + 63 + 31) / 32 + d->max_s + 1;
   d->bm_words = (p->n + 63 + 31) / 32;
+  d->bits_words = (p->slash_tile == 1 && d->has_vs) ? minf::exact_bits_words(p->n) : 0;
   return MINF_OK;
 }
 
@@ -231,6 +232,7 @@ minf_status minf_query_sizes(const minf_problem* prob, const minf_head_cfg* head
   out->max_kb = d.max_kb;
   out->max_chunks = d.max_chunks;
   out->ws_bytes = (int64_t)ws_total(prob, d);
+  out->bits_words = d.bits_words;
   return MINF_OK;
 }
 
@@ -291,6 +293,8 @@ minf_status minf_build_tiles(const minf_problem* prob, const minf_head_cfg* head
                    !tiles->chunk_lo || !tiles->chunk_hi || !tiles->chunk_cnt || !tiles->cols || !tiles->col_cnt))
     return fail(MINF_EINVAL, "a Vertical-Slash head needs vert_idx, slash_idx and every span/chunk/column buffer");
   if (d.has_bs && (!blk_idx || !blk_cnt)) return fail(MINF_EINVAL, "a Block-Sparse head needs blk_idx and blk_cnt");
+  if (d.bits_words > 0 && (!tiles->slash_bits || !tiles->col_bits))
+    return fail(MINF_EINVAL, "slash_tile=1 with a Vertical-Slash head needs slash_bits and col_bits");
   if ((s = check_ws(prob, d, ws, ws_bytes)) != MINF_OK) return s;
   const TilesWs w = tiles_ws(prob, d);
   char* base = static_cast<char*>(ws);
@@ -302,6 +306,7 @@ minf_status minf_build_tiles(const minf_problem* prob, const minf_head_cfg* head
   t.bitmap = reinterpret_cast<uint32_t*>(base + w.bitmap);
   t.head_ok = reinterpret_cast<int32_t*>(base + w.head_ok);
   t.max_v = d.max_v; t.max_s = d.max_s; t.max_kb = d.max_kb; t.max_chunks = d.max_chunks; t.bm_words = d.bm_words;
+  t.bits_words = d.bits_words; t.slash_tile = prob->slash_tile;
   t.B = prob->B; t.Hq = prob->Hq; t.n = prob->n; t.nq = (int)d.nq;
   t.ht = d.ht;
   return hip_status(minf::launch_tiles(t, d.has_vs, d.has_bs, static_cast<hipStream_t>(stream)),
@@ -318,6 +323,8 @@ minf_status minf_sparse_attn(const minf_problem* prob, const minf_head_cfg* head
   if (d.has_bs && (!blk_idx || !blk_cnt)) return fail(MINF_EINVAL, "a Block-Sparse head needs blk_idx and blk_cnt");
   if (d.has_vs && (!tiles || !tiles->chunk_lo || !tiles->chunk_hi || !tiles->chunk_cnt || !tiles->cols || !tiles->col_cnt))
     return fail(MINF_EINVAL, "a Vertical-Slash head needs the tile lists from minf_build_tiles");
+  if (d.bits_words > 0 && (!tiles->slash_bits || !tiles->col_bits))
+    return fail(MINF_EINVAL, "slash_tile=1 with a Vertical-Slash head needs slash_bits and col_bits");
   if ((s = check_ws(prob, d, ws, ws_bytes)) != MINF_OK) return s;
   const AttnWs w = attn_ws(prob, d);
   minf::AttnParams a{};
@@ -342,6 +349,12 @@ minf_status minf_sparse_attn(const minf_problem* prob, const minf_head_cfg* head
   a.n_segs = prob->B * a.n_utiles * prob->Hkv;
   a.c = d.scale * minf::kLog2e;
   a.out_bf16 = prob->out_dtype == MINF_BF16;
+  a.slash_tile = prob->slash_tile;
+  if (d.bits_words > 0) {
+    a.slash_bits = tiles->slash_bits;
+    a.col_bits = tiles->col_bits;
+    a.bits_words = d.bits_words;
+  }
   a.ht = d.ht;
   return hip_status(minf::launch_attn(a, prob->in_dtype == MINF_BF16, prob->dh, static_cast<hipStream_t>(stream)),
                     "minf_sparse_attn launch");

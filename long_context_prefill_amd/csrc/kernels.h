@@ -6,6 +6,12 @@
 
 namespace minf {
 
+// Left padding, in bits, of the exact-slash bitmaps (minf_tiles.slash_bits,
+// col_bits): offset d sits at bit n + kBitsPad - 1 - d, column j at bit
+// j + kBitsPad, so every 32-bit window a chunk needs starts at bit >= 0.
+constexpr int kBitsPad = 128;
+inline int64_t exact_bits_words(int n) { return ((int64_t)n + 2 * kBitsPad + 64 + 31) / 32 + 2; }
+
 // ---------------------------------------------------------------- attention
 struct AttnParams {
   const void* Q;
@@ -35,8 +41,12 @@ struct AttnParams {
   int32_t* queue;           // ws [B*Hq*nq]: items b*Hq*nq + h*nq + u
   int32_t* queue_meta;      // ws [24]: queue offsets, counts, counters per XCD
   int32_t sched_P, sched_R, sched_units;
+  // exact slash pairs (slash_tile == 1): per-head bitmaps from the tile stage
+  int32_t slash_tile;
+  const uint32_t* slash_bits;   // [B,Hq,bits_words]: bit n + kBitsPad - 1 - d set iff d in D_h
+  const uint32_t* col_bits;     // [B,Hq,bits_words]: bit j + kBitsPad set iff j in C_h
+  int64_t bits_words;
 };
-// Units of the attention schedule for B*Hq heads and nq query blocks.
 // Units of the bf16 attention schedule: each head's query blocks are cut
 // into P runs of R consecutive blocks.  About kUnitsPerGroup units per KV
 // group, so that one group's work spreads evenly over the eight XCD queues
@@ -78,6 +88,8 @@ struct TileParams {
   uint32_t* bitmap;          // ws [B,Hq,bm_words]: bit x+63 set iff x in S
   int32_t* head_ok;          // ws [B,Hq]
   int64_t max_v, max_s, max_kb, max_chunks, bm_words;
+  int64_t bits_words;        // words of t.slash_bits / t.col_bits (slash_tile == 1)
+  int32_t slash_tile;
   int32_t B, Hq, n, nq;
   HeadTable ht;              // ASHAPE: a = sink, b = window; VSLASH: b = #columns, c = #offsets
 };

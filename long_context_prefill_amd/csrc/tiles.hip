@@ -17,7 +17,11 @@
 // Kept edges E_h = sum_i |N_h(i)| (section 1.2 of the page) are counted in
 // closed form per query block: slash keys through prefix counts of S, plus
 // the uncovered verticals, plus the block areas of Block-Sparse heads, plus
-// the A-shape formula sum_i min(i+1, g+w) (Eq. 4).
+// the A-shape formula sum_i min(i+1, g+w) (Eq. 4).  Under exact slash pairs
+// (slash_tile == 1, Eq. 5 taken literally) the tile lists stay the same (the
+// pairs of offset d in block u lie inside [64u - d, 64u + 63 - d]); the
+// attention then tests each pair against per-head offset and column
+// bitmaps, and E_h is counted from the two sorted lists.
 #include "kernels.h"
 
 namespace minf {
@@ -230,6 +234,7 @@ __global__ __launch_bounds__(256) void vs_cols_kernel(TileParams P) {
       if (__any(!in_range)) break;   // columns are ascending: the rest lie beyond the block
     }
     if (lane == 0) P.t.col_cnt[bu] = cnt;
+    if (P.slash_tile == 1) edges = 0;   // exact slash pairs: counted by vs_exact_edges_kernel
   }
   // reduce edges over the work-group, one atomic per group (integer: order-free)
   for (int off = 32; off > 0; off >>= 1) edges += __shfl_xor(edges, off);
@@ -238,6 +243,72 @@ __global__ __launch_bounds__(256) void vs_cols_kernel(TileParams P) {
   if (threadIdx.x == 0) {
     const unsigned long long tot = part[0] + part[1] + part[2] + part[3];
     if (tot) atomicAdd(reinterpret_cast<unsigned long long*>(P.t.kept_edges + bh), tot);
+  }
+}
+
+// 3b) exact slash pairs (slash_tile == 1, Eq. 5): the per-head bitmaps the
+//     attention tests each span pair against.  Bit n + kBitsPad - 1 - d of
+//     slash_bits marks offset d, bit j + kBitsPad of col_bits column j.
+//     One thread per 32-bit word, both lists ascending.
+__device__ __forceinline__ int lower_bound_i32(const int32_t* a, int cnt, int x) {
+  int l = 0, r = cnt;
+  while (l < r) { const int m = (l + r) >> 1; if (a[m] < x) l = m + 1; else r = m; }
+  return l;
+}
+
+__global__ __launch_bounds__(256) void vs_bits_kernel(TileParams P) {
+  const int bh = blockIdx.y;
+  const int h = bh % P.Hq;
+  if (P.ht.kind[h] != MINF_VSLASH) return;
+  const int64_t w = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (w >= P.bits_words) return;
+  const bool ok = P.head_ok[bh] != 0;
+  uint32_t sb = 0, cb = 0;
+  if (ok) {
+    const int n = P.n;
+    const int b0 = (int)(32 * w);
+    // offsets d with bit n + kBitsPad - 1 - d in [b0, b0 + 31]
+    const int ns = P.ht.c[h];
+    const int32_t* offs = P.slash_idx + (size_t)bh * P.max_s;
+    const int dlo = n + kBitsPad - 1 - (b0 + 31), dhi = n + kBitsPad - 1 - b0;
+    for (int k = lower_bound_i32(offs, ns, dlo); k < ns && offs[k] <= dhi; ++k)
+      sb |= 1u << (n + kBitsPad - 1 - offs[k] - b0);
+    // columns j with bit j + kBitsPad in [b0, b0 + 31]
+    const int nv = P.ht.b[h];
+    const int32_t* cols = P.vert_idx + (size_t)bh * P.max_v;
+    const int jlo = b0 - kBitsPad, jhi = b0 - kBitsPad + 31;
+    for (int k = lower_bound_i32(cols, nv, jlo); k < nv && cols[k] <= jhi; ++k)
+      cb |= 1u << (cols[k] + kBitsPad - b0);
+  }
+  P.t.slash_bits[(size_t)bh * P.bits_words + w] = sb;
+  P.t.col_bits[(size_t)bh * P.bits_words + w] = cb;
+}
+
+// 3c) kept edges under exact slash pairs: sum_i |{j <= i : i - j in D} u
+//     {j <= i : j in C}| = sum_d (n - d) + sum_c (n - c) - #{(c, d) : c + d <= n-1}.
+__global__ __launch_bounds__(256) void vs_exact_edges_kernel(TileParams P) {
+  const int bh = blockIdx.x;
+  const int h = bh % P.Hq;
+  if (P.ht.kind[h] != MINF_VSLASH || !P.head_ok[bh]) return;
+  const int n = P.n;
+  const int ns = P.ht.c[h], nv = P.ht.b[h];
+  const int32_t* offs = P.slash_idx + (size_t)bh * P.max_s;
+  const int32_t* cols = P.vert_idx + (size_t)bh * P.max_v;
+  long long e = 0;
+  for (int k = threadIdx.x; k < ns; k += 256) e += n - offs[k];
+  for (int k = threadIdx.x; k < nv; k += 256) {
+    const int c = cols[k];
+    // offsets d <= n - 1 - c: pairs (c, d) whose key c is also at offset d of row c + d
+    const int both = lower_bound_i32(offs, ns, n - c);
+    e += (long long)(n - c) - both;
+  }
+  __shared__ long long part[4];
+  for (int off = 32; off > 0; off >>= 1) e += __shfl_xor(e, off);
+  if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = e;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const long long tot = part[0] + part[1] + part[2] + part[3];
+    atomicAdd(reinterpret_cast<unsigned long long*>(P.t.kept_edges + bh), (unsigned long long)tot);
   }
 }
 
@@ -279,6 +350,10 @@ hipError_t launch_tiles(const TileParams& p, bool has_vs, bool has_bs, hipStream
   if (has_vs) {
     hipLaunchKernelGGL(vs_chunks_kernel, dim3(BH), dim3(256), 0, st, p);
     hipLaunchKernelGGL(vs_cols_kernel, dim3((p.nq + 3) / 4, BH), dim3(256), 0, st, p);
+    if (p.slash_tile == 1) {
+      hipLaunchKernelGGL(vs_bits_kernel, dim3((unsigned)((p.bits_words + 255) / 256), BH), dim3(256), 0, st, p);
+      hipLaunchKernelGGL(vs_exact_edges_kernel, dim3(BH), dim3(256), 0, st, p);
+    }
   }
   if (has_bs) hipLaunchKernelGGL(bs_edges_kernel, dim3((p.nq + 255) / 256, BH), dim3(256), 0, st, p);
   return hipGetLastError();

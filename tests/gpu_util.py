@@ -96,8 +96,12 @@ def check_selection(gpu_idx, scores, k, what):
     return int(diff.shape[0]), int(near.sum())
 
 
-def check_tiles(p, res, buf, slash_tile=64):
-    """Exact checks of the GPU tile lists against the oracle's index sets."""
+def check_tiles(p, res, buf):
+    """Exact checks of the GPU tile lists against the oracle's index sets.
+    The lists are the 64-row slash expansion under either slash_tile (exact
+    pairs only add a per-pair test); kept edges follow the oracle run's
+    slash_tile."""
+    slash_tile = 64
     sz = buf["sizes"]
     t = {k: v.cpu().numpy() for k, v in buf["tiles"].items()}
     n, nq = p.n, int(sz.nq)

@@ -38,8 +38,8 @@ def test_exports_every_declared_symbol(lib):
 def test_struct_layouts_match_header():
     assert ctypes.sizeof(M.MinfProblem) == 40
     assert ctypes.sizeof(M.MinfHeadCfg) == 32
-    assert ctypes.sizeof(M.MinfSizes) == 48
-    assert ctypes.sizeof(M.MinfTiles) == 80
+    assert ctypes.sizeof(M.MinfSizes) == 56
+    assert ctypes.sizeof(M.MinfTiles) == 96
 
 
 def _prob(**kw):
@@ -59,6 +59,19 @@ def test_query_sizes(lib):
     assert s.max_kb == 4
     assert s.max_chunks == (1000 + 63 + 31) // 32 + 1000 + 1
     assert s.ws_bytes > 0
+    assert s.bits_words == 0        # only for exact slash pairs
+
+
+def test_query_sizes_exact_slash_pairs(lib):
+    """slash_tile=1 (Eq. 5 pairs) sizes the two per-head bitmaps: offset d
+    at bit n + 127 - d, column j at bit j + 128, 32-bit words, with room for
+    the three-word windows the attention reads."""
+    s = M.minf_query_sizes(_prob(slash_tile=1), M.make_heads(HEADS))
+    assert s.bits_words == (1000 + 2 * 128 + 64 + 31) // 32 + 2
+    assert s.bits_words * 32 >= 1000 + 128 + 128 + 64
+    # no Vertical-Slash head: no bitmaps
+    s = M.minf_query_sizes(_prob(slash_tile=1), M.make_heads([gen.ashape(4, 8)] * 4))
+    assert s.bits_words == 0
 
 
 @pytest.mark.parametrize("kw,heads,status", [
@@ -66,7 +79,6 @@ def test_query_sizes(lib):
     (dict(dh=96), HEADS, M.MINF_EUNSUPPORTED),
     (dict(n=0), HEADS, M.MINF_EINVAL),
     (dict(block=32), HEADS, M.MINF_EUNSUPPORTED),
-    (dict(slash_tile=1), HEADS, M.MINF_EUNSUPPORTED),
     (dict(slash_tile=16), HEADS, M.MINF_EINVAL),
     (dict(scale=-1.0), HEADS, M.MINF_EINVAL),
     (dict(), [gen.ashape(-1, 3)] + HEADS[1:], M.MINF_EINVAL),
@@ -106,6 +118,14 @@ def test_calls_reject_before_launch(lib):
                               fake, 1 << 40, None)
     assert st == M.MINF_EINVAL          # VS head without tile lists
     assert "tile" in lib.minf_last_error().decode()
+    # exact slash pairs need the two bitmaps
+    p1 = _prob(slash_tile=1)
+    ts = M.MinfTiles(*([fake] * 10 + [None, None]))
+    st = lib.minf_build_tiles(ctypes.byref(p1), h, fake, fake, fake, fake, ctypes.byref(ts), fake, 1 << 40, None)
+    assert st == M.MINF_EINVAL and "slash_bits" in lib.minf_last_error().decode()
+    st = lib.minf_sparse_attn(ctypes.byref(p1), h, fake, fake, fake, fake, fake, ctypes.byref(ts), fake, None,
+                              fake, 1 << 40, None)
+    assert st == M.MINF_EINVAL and "slash_bits" in lib.minf_last_error().decode()
 
 
 def test_no_work_for_absent_kinds(lib):

@@ -168,3 +168,39 @@ def test_full_size_layer(w):
             ref = _row_refs(q, _Widened(k), _Widened(v), rows, keys_fn, sc, what)
         U.compare_output(og, ref, p.dtype, f"{what}, {len(rows)} rows")
         U.log(f"  {what}: done ({time.time() - t0:.0f}s)")
+
+
+@pytest.mark.timeout(400)
+def test_full_size_exact_slash_pairs():
+    """The 128K mixed layer with slash_tile=1 (Eq. 5 pairs): one
+    Vertical-Slash head's kept edges against the oracle's count over the
+    GPU's own index sets, and its 4096 sampled + edge rows against the
+    oracle's restricted softmax over the exact-pair key sets."""
+    import torch
+    t0 = time.time()
+    p = gen.make_workload(3)
+    n, g, sc = p.n, p.Hq // p.Hkv, p.eff_scale
+    prob = M.make_problem(p.B, p.Hq, p.Hkv, p.n, p.dh, p.dtype, "f32", p.scale, slash_tile=1)
+    heads = M.make_heads(p.heads)
+    buf = M.alloc_buffers(prob, heads)
+    Q, K, V = U.device_inputs(p)
+    Og = torch.empty((p.B, p.Hq, n, p.dh), dtype=torch.float32, device="cuda")
+    t = buf["tiles"]
+    M.run_layer(prob, heads, Q, K, V, Og, buf=buf)
+    torch.cuda.synchronize()
+    assert int(t["status"].item()) == 0
+    h = next(h for h, c in enumerate(p.heads) if c.kind == gen.VSLASH)
+    vi = buf["vert_idx"][0, h].cpu().numpy()
+    si = buf["slash_idx"][0, h].cpu().numpy()
+    cols, offs = vi[vi >= 0].astype(np.int64), si[si >= 0].astype(np.int64)
+    assert int(t["kept_edges"][0, h].item()) == O.vs_edges(n, cols, offs, 1)
+    U.log(f"  exact pairs: head {h} kept edges match ({time.time() - t0:.0f}s)")
+    cover = O.slash_offset_set(offs, n, 1)
+    rows = np.unique(np.concatenate([p.rows, p.edge_rows])).astype(np.int64)
+    q = _f32(p.Q[0, h], p.dtype)
+    k = _f32(p.K[0, h // g], p.dtype)
+    v = _f32(p.V[0, h // g], p.dtype)
+    og = Og[0, h][torch.from_numpy(rows).cuda()].cpu().numpy()
+    ref = _row_refs(q, _Widened(k), _Widened(v), rows, lambda i: O.vs_row_keys(i, cols, cover, 1), sc,
+                    f"head {h} exact pairs")
+    U.compare_output(og, ref, p.dtype, f"128K head {h} exact pairs, {len(rows)} rows")

@@ -39,9 +39,10 @@ def _small_cases():
 CASES = _small_cases()
 
 
-def _run_attn_given(p, res, out_dtype="f32"):
+def _run_attn_given(p, res, out_dtype="f32", slash_tile=64):
     import torch
     prob = U.make_prob(p, out_dtype)
+    prob.slash_tile = slash_tile
     heads = M.make_heads(p.heads)
     buf = M.alloc_buffers(prob, heads)
     U.load_oracle_indices(p, res, buf)
@@ -233,3 +234,23 @@ def test_dense_causal_baseline_as_full_window(n):
         v = O.widen(p.V[0, h // g], p.dtype)
         ref[0, h], _ = O.dense_attention(q, k, v, p.eff_scale)
     U.compare_output(Og, ref, p.dtype, f"dense n={n}")
+
+
+EXACT_CASES = ["n1000_h8kv2_d128_bf16", "n333_b2_h4kv1_d64_bf16", "n700_h4kv2_d128_f32", "n4100_h4kv1_d128_bf16_iid"]
+
+
+@pytest.mark.parametrize("name", EXACT_CASES)
+def test_exact_slash_pairs_given_oracle_indices(name):
+    """slash_tile=1: Eq. 5 taken literally (row i keeps key j iff i - j is a
+    selected offset or j a selected column, j <= i).  Same tile lists; kept
+    edges and every output row against the oracle run with slash_tile=1."""
+    U.log(f"exact case {name}")
+    p = CASES[name]()
+    res = O.run_layer(p.Q, p.K, p.V, p.dtype, p.heads, scale=p.scale, slash_tile=1)
+    buf, Og, lse = _run_attn_given(p, res, slash_tile=1)
+    U.check_tiles(p, res, buf)
+    U.compare_output(Og, res["O"], p.dtype, f"{name} O (exact pairs)")
+    fin = np.isfinite(res["LSE"])
+    assert np.array_equal(np.isfinite(lse), fin), "empty rows differ"
+    assert np.abs(lse[fin] - res["LSE"][fin]).max(initial=0.0) < (2e-2 if p.dtype == "bf16" else 1e-5)
+    assert np.all(Og[~fin] == 0)
