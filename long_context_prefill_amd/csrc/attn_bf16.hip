@@ -605,9 +605,10 @@ __device__ __forceinline__ void attn_item(const AttnParams& P, const int b, cons
   //   ascending walk at 128K, and equal at 1M);
   // * A-shape: block u's window is block (u+1)'s shifted down by two chunks,
   //   so the walk starts two chunks further along per dispatch position;
-  // * Block-Sparse: selected blocks in ascending order.
-  const int step = 1;
-  int kc = KIND == MINF_ASHAPE ? (2 * (slot & 127)) % C : 0;
+  // * Block-Sparse: selected blocks from the last (the diagonal) down
+  //   (3.4% faster than ascending at 512K).
+  const int step = KIND == MINF_BSPARSE ? -1 : 1;
+  int kc = KIND == MINF_ASHAPE ? (2 * (slot & 127)) % C : (KIND == MINF_BSPARSE ? C - 1 : 0);
   auto advance = [&]() {
     kc += step;
     kc = kc == C ? 0 : (kc < 0 ? C - 1 : kc);
