@@ -367,11 +367,11 @@ def main():
     dense = p.B * p.Hq * p.n * (p.n + 1) // 2
     computed = computed_pairs(p, t, buf)
 
-    dense = None
+    dense_bl = None
     if not a.no_dense:
         t0 = time.time()
         ms_d, kept_d = time_layer(M, prob, M.make_heads(dense_heads(p.Hq, p.n)), Q, K, V, O_, 3, 1, False, flush)
-        dense = {"ms": round(ms_d, 3), "kept_edges": kept_d,
+        dense_bl = {"ms": round(ms_d, 3), "kept_edges": kept_d,
                  "tflops": round(4 * p.dh * kept_d / (ms_d * 1e-3) / 1e12, 1),
                  "speedup_of_sparse": round(ms_d / ms_step, 3),
                  "what": "same inputs, every head A-shape(sink 0, window n) = all j <= i; tile build + attention, "
@@ -439,7 +439,7 @@ def main():
                      "kernel": ATTN_KERNEL if (p.dtype == "bf16" and p.dh == 128) else "attn_kernel",
                      "per_launch_flops": flops, "avg_launch_ms": round(ms_kernel, 4),
                      "launches_timed": len(kern)},
-        "dense_baseline": dense,
+        "dense_baseline": dense_bl,
         "exact_slash_pairs": exact,
         "cpu_baseline": cpu,
         "context": "pages: up to 10x prefill speedup over dense on an A100 (another machine and workload)",

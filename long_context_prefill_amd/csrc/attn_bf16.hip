@@ -215,6 +215,11 @@ __global__ __launch_bounds__(256) void attn_cost_kernel(AttnParams P) {
 
 __global__ __launch_bounds__(256) void attn_sched_kernel(AttnParams P) {
   const int U = P.sched_units;
+  // the greedy pass below is serial: its inputs are staged in LDS when they
+  // fit (units beyond kMaxUnits only arise for more than kMaxUnits (batch,
+  // head) pairs, and are then read from global memory)
+  __shared__ int s_order[kMaxUnits], s_cost[kMaxUnits], s_items[kMaxUnits];
+  const bool staged = U <= kMaxUnits;
   // The units of one KV group are contiguous (heads g0 .. g0 + gsz - 1 of one
   // batch entry); rank them by (group ascending, cost descending, unit
   // ascending), comparing within the group only.
@@ -228,6 +233,12 @@ __global__ __launch_bounds__(256) void attn_sched_kernel(AttnParams P) {
       r += (cv > cu) || (cv == cu && v < u);
     }
     P.sched_order[r] = u;
+    if (staged) {
+      s_order[r] = u;
+      s_cost[u] = (int)min(cu, (long long)0x7fffffff);
+      int u0, u1, nbs;
+      s_items[u] = unit_items(P, u, &u0, &u1, &nbs);
+    }
   }
   __syncthreads();
   if (threadIdx.x == 0) {
@@ -235,16 +246,25 @@ __global__ __launch_bounds__(256) void attn_sched_kernel(AttnParams P) {
     int cnt[8];
     for (int x = 0; x < 8; ++x) { load[x] = 0; cnt[x] = 0; }
     for (int i = 0; i < U; ++i) {
-      const int unit = P.sched_order[i];
-      const long long cu = P.sched_cost[unit];
+      int unit, items;
+      long long cu;
+      if (staged) {
+        unit = s_order[i];
+        cu = s_cost[unit];
+        items = s_items[unit];
+      } else {
+        unit = P.sched_order[i];
+        cu = P.sched_cost[unit];
+        int u0, u1, nbs;
+        items = unit_items(P, unit, &u0, &u1, &nbs);
+      }
       if (cu < 0) { P.unit_xcd[unit] = -1; continue; }
       int best = 0;
       for (int x = 1; x < 8; ++x)
         if (load[x] < load[best]) best = x;
-      int u0, u1, nbs;
       P.unit_xcd[unit] = best;
       P.unit_off[unit] = cnt[best];
-      cnt[best] += unit_items(P, unit, &u0, &u1, &nbs);
+      cnt[best] += items;
       load[best] += cu;
     }
     int off = 0;

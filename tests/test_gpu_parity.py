@@ -254,3 +254,16 @@ def test_exact_slash_pairs_given_oracle_indices(name):
     assert np.array_equal(np.isfinite(lse), fin), "empty rows differ"
     assert np.abs(lse[fin] - res["LSE"][fin]).max(initial=0.0) < (2e-2 if p.dtype == "bf16" else 1e-5)
     assert np.all(Og[~fin] == 0)
+
+
+def test_many_batch_heads():
+    """More (batch, head) pairs than the attention scheduler stages in LDS
+    (B * Hq = 4160 > 4096 units): the schedule falls back to global memory;
+    every kind, ragged n, against the oracle."""
+    U.log("many batch x heads")
+    base = [gen.ashape(16, 40), gen.vslash(32, 8, 16), gen.bsparse(2), gen.vslash(16, 4, 4)]
+    p = gen.make_small(n=150, B=65, Hq=64, Hkv=16, dh=128, seed=31, heads=[base[h % 4] for h in range(64)])
+    res = O.run_layer(p.Q, p.K, p.V, p.dtype, p.heads, scale=p.scale)
+    buf, Og, lse = _run_attn_given(p, res)
+    U.check_tiles(p, res, buf)
+    U.compare_output(Og, res["O"], p.dtype, "B=65 Hq=64 O")
