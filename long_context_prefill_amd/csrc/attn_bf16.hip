@@ -146,9 +146,10 @@ __device__ __forceinline__ ItemLists item_lists(const AttnParams& P, size_t bh, 
 //   group) over such a run, interleaved per query block: heads that share K
 //   and V and select nearly the same key blocks run side by side.
 // Units are costed by their exact chunk counts.  KV groups are taken in
-// order, and within a group the units are assigned largest first to the
-// least-loaded XCD, so the eight XCDs work through the groups together and
-// the active group's K and V stay in the memory-side cache.  The
+// order, and within a group the units are handed out largest first, eight
+// at a time, to the eight XCD queues in ascending order of load, so the
+// XCDs work through the groups
+// together (the active group's K and V stay in the memory-side cache).  The
 // work-groups that run together on one XCD are consecutive query blocks of
 // one head (or one KV group), whose key sets largely coincide, so their K/V
 // rows are also shared in that XCD's L2.
@@ -215,65 +216,86 @@ __global__ __launch_bounds__(256) void attn_cost_kernel(AttnParams P) {
 
 __global__ __launch_bounds__(256) void attn_sched_kernel(AttnParams P) {
   const int U = P.sched_units;
-  // the greedy pass below is serial: its inputs are staged in LDS when they
-  // fit (units beyond kMaxUnits only arise for more than kMaxUnits (batch,
-  // head) pairs, and are then read from global memory)
-  __shared__ int s_order[kMaxUnits], s_cost[kMaxUnits], s_items[kMaxUnits];
-  const bool staged = U <= kMaxUnits;
+  const int tid = threadIdx.x, lane = tid & 63;
   // The units of one KV group are contiguous (heads g0 .. g0 + gsz - 1 of one
   // batch entry); rank them by (group ascending, cost descending, unit
-  // ascending), comparing within the group only.
+  // ascending), comparing within the group only.  Queue order is rank order.
   const int per_group = P.gsz * P.sched_P;
-  for (int u = threadIdx.x; u < U; u += 256) {
+  __shared__ int s_unit[kMaxUnits], s_cost[kMaxUnits], s_items[kMaxUnits];
+  const bool staged = U <= kMaxUnits;   // beyond kMaxUnits units: global memory
+  for (int u = tid; u < U; u += 256) {
     const long long cu = P.sched_cost[u];
     const int g0 = u - u % per_group;
     int r = g0;
+    #pragma unroll 8
     for (int v = g0; v < g0 + per_group; ++v) {
       const long long cv = P.sched_cost[v];
       r += (cv > cu) || (cv == cu && v < u);
     }
     P.sched_order[r] = u;
     if (staged) {
-      s_order[r] = u;
-      s_cost[u] = (int)min(cu, (long long)0x7fffffff);
       int u0, u1, nbs;
-      s_items[u] = unit_items(P, u, &u0, &u1, &nbs);
+      s_unit[r] = u;
+      s_cost[r] = (int)min(cu, (long long)0x7fffffff);
+      s_items[r] = unit_items(P, u, &u0, &u1, &nbs);
     }
   }
   __syncthreads();
-  if (threadIdx.x == 0) {
-    long long load[8];
-    int cnt[8];
-    for (int x = 0; x < 8; ++x) { load[x] = 0; cnt[x] = 0; }
-    for (int i = 0; i < U; ++i) {
-      int unit, items;
-      long long cu;
-      if (staged) {
-        unit = s_order[i];
-        cu = s_cost[unit];
-        items = s_items[unit];
-      } else {
-        unit = P.sched_order[i];
-        cu = P.sched_cost[unit];
-        int u0, u1, nbs;
-        items = unit_items(P, unit, &u0, &u1, &nbs);
+  if (tid >= 64) return;
+  // Greedy pass on one wave, eight units at a time: lane x < 8 holds XCD
+  // x's load and item count; each round of a group hands its next eight
+  // units (largest first) to the eight XCDs in ascending order of load
+  // (ties to the lower index), the least-loaded XCD taking the largest unit.
+  long long myload = 0;
+  int mycnt = 0;
+  for (int g0 = 0; g0 < U; g0 += per_group) {
+    for (int j0 = 0; j0 < per_group; j0 += 8) {
+      // this lane's XCD rank by load (readlane with constant lanes: no LDS)
+      int rank = 0;
+      #pragma unroll
+      for (int y = 0; y < 8; ++y) {
+        const int lo32 = __builtin_amdgcn_readlane((int)(uint32_t)myload, y);
+        const int hi32 = __builtin_amdgcn_readlane((int)(myload >> 32), y);
+        const long long ly = ((long long)hi32 << 32) | (uint32_t)lo32;
+        rank += (ly < myload) || (ly == myload && y < lane);
       }
-      if (cu < 0) { P.unit_xcd[unit] = -1; continue; }
-      int best = 0;
-      for (int x = 1; x < 8; ++x)
-        if (load[x] < load[best]) best = x;
-      P.unit_xcd[unit] = best;
-      P.unit_off[unit] = cnt[best];
-      cnt[best] += items;
-      load[best] += cu;
+      const int j = j0 + rank;
+      if (lane < 8 && j < per_group) {
+        const int o = g0 + j;
+        int unit, items;
+        long long cu;
+        if (staged) {
+          unit = s_unit[o];
+          cu = s_cost[o];
+          items = s_items[o];
+        } else {
+          unit = P.sched_order[o];
+          cu = P.sched_cost[unit];
+          int u0, u1, nbs;
+          items = unit_items(P, unit, &u0, &u1, &nbs);
+        }
+        if (cu < 0) {
+          P.unit_xcd[unit] = -1;
+        } else {
+          P.unit_xcd[unit] = lane;
+          P.unit_off[unit] = mycnt;
+          mycnt += items;
+          myload += cu;
+        }
+      }
     }
-    int off = 0;
-    for (int x = 0; x < 8; ++x) {
-      P.queue_meta[x] = off;
-      P.queue_meta[8 + x] = cnt[x];
-      P.queue_meta[16 + x] = 0;     // the queue counters start at zero
-      off += cnt[x];
-    }
+  }
+  // queue offsets: exclusive sum of the item counts over lanes 0..7
+  int incl = lane < 8 ? mycnt : 0;
+  #pragma unroll
+  for (int off = 1; off < 8; off <<= 1) {
+    const int y = __shfl_up(incl, off);
+    if (lane >= off) incl += y;
+  }
+  if (lane < 8) {
+    P.queue_meta[lane] = incl - mycnt;
+    P.queue_meta[8 + lane] = mycnt;
+    P.queue_meta[16 + lane] = 0;     // the queue counters start at zero
   }
 }
 

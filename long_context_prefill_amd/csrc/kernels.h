@@ -100,9 +100,13 @@ constexpr int kVsWaveKeys = 256;                  // keys per wave in the proxy 
 constexpr int kVsGroupKeys = 4 * kVsWaveKeys;     // keys per work-group
 constexpr int kVsDiagSlots = kVsWaveKeys + 64;    // diagonal partials per wave
 
+constexpr int kTopkSeg = 8192;                    // array elements per top-k work-group
 struct VsWs {
-  size_t part_m, part_l, lse2, cbuf, rbuf, dpart, total;
+  size_t part_m, part_l, lse2, cbuf, rbuf, dpart;
+  size_t tk_state, tk_hist, tk_cnt;               // multi-work-group top-k of c and r
+  size_t total;
   int64_t nslots;                                 // proxy waves per head
+  int64_t tk_segs;                                // segments of an n-element array
 };
 VsWs vs_workspace(int B, int Hq, int n, int nq);
 

@@ -204,15 +204,15 @@ __global__ __launch_bounds__(256) void vs_cols_kernel(TileParams P) {
       cov_pos = cum[rs] + (e >= s ? e - s + 1 : 0);
     }
     ccnt = min<long long>(ccnt, P.max_chunks);
-    // span edges: Lu per covered x >= 0 with x <= 64u, and max(0, Lu + x) for x in [-63, -1]
+    // span edges: Lu per covered x >= 0 with x <= 64u, and max(0, Lu + x)
+    // for x in [-63, -1] (lane l takes x = l - 63)
     if (lane == 0) {
-      long long e = (long long)Lu * cov_pos;
-      if (nr > 0) {
-        for (int x = -63; x <= -1; ++x)
-          if (Lu + x > 0 && covered(bm, x)) e += Lu + x;
-      }
-      edges += e;
+      edges += (long long)Lu * cov_pos;
       P.t.chunk_cnt[bu] = ccnt;
+    }
+    if (nr > 0 && lane < 63) {
+      const int x = lane - 63;
+      if (Lu + x > 0 && covered(bm, x)) edges += Lu + x;
     }
     // uncovered verticals of this block, ascending
     const int nv = ok ? P.ht.b[h] : 0;

@@ -40,6 +40,10 @@ VsWs vs_workspace(int B, int Hq, int n, int nq) {
   w.cbuf = take(BH * (size_t)n * 4);
   w.rbuf = take(BH * (size_t)n * 4);
   w.dpart = take(BH * w.nslots * kVsDiagSlots * 4);
+  w.tk_segs = ((int64_t)n + kTopkSeg - 1) / kTopkSeg;
+  w.tk_state = take(2 * BH * 4 * 4);
+  w.tk_hist = take(2 * BH * w.tk_segs * 256 * 4);
+  w.tk_cnt = take(2 * BH * w.tk_segs * 2 * 4);
   w.total = off;
   return w;
 }
@@ -307,29 +311,209 @@ __global__ __launch_bounds__(256) void vs_diag_kernel(VsParams P) {
   rdst[(size_t)bh * n + d] = acc;
 }
 
-// Top-v columns / top-s offsets, one work-group per (head, array).
-__global__ __launch_bounds__(1024) void vs_topk_kernel(VsParams P) {
-  const int bh = blockIdx.x >> 1;
-  const int which = blockIdx.x & 1;
-  const int h = bh % P.Hq;
-  if (P.ht.kind[h] != MINF_VSLASH) return;
-  __shared__ TopkShared sh;
-  const int n = P.n;
+// Top-v columns / top-s offsets (selection order: score descending, index
+// ascending; outputs ascending), the same radix select as topk.h spread over
+// kTopkSeg-element segments of each array: array a = 2 * bh + which (which
+// 0: c -> vert_idx, 1: r -> slash_idx).  Per array the workspace holds the
+// select state {prefix, mask, remaining}, 256 bins per segment and
+// per-segment (greater, equal) counts; kernel boundaries order the passes.
+struct TkArray {
   const float* src;
   int32_t* out;
   int k, cap;
+  bool vs;
+};
+__device__ __forceinline__ TkArray tk_array(const VsParams& P, int a) {
+  const int bh = a >> 1, which = a & 1;
+  const int h = bh % P.Hq;
+  TkArray t;
+  t.vs = P.ht.kind[h] == MINF_VSLASH;
   if (which == 0) {
-    src = (P.vert_score ? P.vert_score : reinterpret_cast<const float*>(P.ws_base + P.ws.cbuf)) + (size_t)bh * n;
-    out = P.vert_idx + (size_t)bh * P.max_v;
-    k = P.ht.b[h];
-    cap = (int)P.max_v;
+    t.src = (P.vert_score ? P.vert_score : reinterpret_cast<const float*>(P.ws_base + P.ws.cbuf)) + (size_t)bh * P.n;
+    t.out = P.vert_idx + (size_t)bh * P.max_v;
+    t.k = min(P.ht.b[h], P.n);
+    t.cap = (int)P.max_v;
   } else {
-    src = (P.slash_score ? P.slash_score : reinterpret_cast<const float*>(P.ws_base + P.ws.rbuf)) + (size_t)bh * n;
-    out = P.slash_idx + (size_t)bh * P.max_s;
-    k = P.ht.c[h];
-    cap = (int)P.max_s;
+    t.src = (P.slash_score ? P.slash_score : reinterpret_cast<const float*>(P.ws_base + P.ws.rbuf)) + (size_t)bh * P.n;
+    t.out = P.slash_idx + (size_t)bh * P.max_s;
+    t.k = min(P.ht.c[h], P.n);
+    t.cap = (int)P.max_s;
   }
-  block_topk_array<1024>(src, n, k, out, cap, sh);
+  return t;
+}
+
+// grid (2 * B * Hq): reset the select state of every array
+__global__ __launch_bounds__(64) void vs_tk_init_kernel(VsParams P) {
+  const int a = blockIdx.x;
+  const TkArray t = tk_array(P, a);
+  if (!t.vs || threadIdx.x != 0) return;
+  int32_t* st = reinterpret_cast<int32_t*>(P.ws_base + P.ws.tk_state) + 4 * a;
+  const bool all = t.k >= P.n;           // take every element: T = 0, all are greater or equal
+  st[0] = 0;                             // prefix
+  st[1] = all ? -1 : 0;                  // mask (all ones when done)
+  st[2] = all ? P.n : t.k;               // remaining (elements equal to T that are taken)
+}
+
+// grid (segments, 2 * B * Hq): histogram of one radix digit (at `shift`)
+// over one segment, for the keys that match the select state so far; each
+// segment writes its own 256 bins.
+__global__ __launch_bounds__(256) void vs_tk_pass_kernel(VsParams P, int shift) {
+  const int seg = blockIdx.x, a = blockIdx.y;
+  const TkArray t = tk_array(P, a);
+  if (!t.vs || t.k <= 0 || t.k >= P.n) return;
+  const int32_t* st = reinterpret_cast<const int32_t*>(P.ws_base + P.ws.tk_state) + 4 * a;
+  int32_t* ghist = reinterpret_cast<int32_t*>(P.ws_base + P.ws.tk_hist) + ((size_t)a * P.ws.tk_segs + seg) * 256;
+  __shared__ int hist[4][256];
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  for (int i = tid; i < 4 * 256; i += 256) hist[i >> 8][i & 255] = 0;
+  const uint32_t prefix = (uint32_t)st[0], mask = (uint32_t)st[1];
+  __syncthreads();
+  const int lo = seg * kTopkSeg, hi = min(lo + kTopkSeg, P.n);
+  // all of the thread's loads are issued before any is used
+  constexpr int E = kTopkSeg / 256;
+  float x[E];
+  #pragma unroll
+  for (int e = 0; e < E; ++e) {
+    const int i = lo + tid + 256 * e;
+    x[e] = i < hi ? t.src[i] : 0.f;
+  }
+  #pragma unroll
+  for (int e = 0; e < E; ++e) {
+    const uint32_t key = order_key(x[e]);
+    const bool m = lo + tid + 256 * e < hi && (key & mask) == prefix;
+    const uint32_t d = (key >> shift) & 255u;
+    // scores of one array cluster in few bins: when every counted lane of
+    // the wave has the same digit, one lane adds them all
+    const unsigned long long act = __ballot(m);
+    if (act == 0ull) continue;
+    const int first = __builtin_ctzll(act);
+    const uint32_t d0 = (uint32_t)__builtin_amdgcn_readlane((int)d, first);
+    const unsigned long long same = __ballot(m && d == d0);
+    if (same == act) {
+      if (lane == first) atomicAdd(&hist[wave][d0], (int)__popcll(act));
+    } else if (m) {
+      atomicAdd(&hist[wave][d], 1);
+    }
+  }
+  __syncthreads();
+  ghist[tid] = hist[0][tid] + hist[1][tid] + hist[2][tid] + hist[3][tid];
+}
+
+// grid (2 * B * Hq): sum the segments' bins and pick the digit
+__global__ __launch_bounds__(256) void vs_tk_pick_kernel(VsParams P, int shift) {
+  const int a = blockIdx.x;
+  const TkArray t = tk_array(P, a);
+  if (!t.vs || t.k <= 0 || t.k >= P.n) return;
+  int32_t* st = reinterpret_cast<int32_t*>(P.ws_base + P.ws.tk_state) + 4 * a;
+  const int32_t* ghist = reinterpret_cast<const int32_t*>(P.ws_base + P.ws.tk_hist) + (size_t)a * P.ws.tk_segs * 256;
+  __shared__ int scan[17];
+  __shared__ uint32_t n_prefix, n_mask;
+  __shared__ int n_rem;
+  const uint32_t prefix = (uint32_t)st[0], mask = (uint32_t)st[1];
+  const int rem = st[2];
+  const int segs = (int)P.ws.tk_segs;
+  int tot = 0;
+  for (int s2 = 0; s2 < segs; ++s2) tot += ghist[(size_t)s2 * 256 + threadIdx.x];
+  pick_digit(tot, rem, prefix, mask, shift, scan, &n_prefix, &n_mask, &n_rem);
+  if (threadIdx.x == 0) {
+    st[0] = (int32_t)n_prefix;
+    st[1] = (int32_t)n_mask;
+    st[2] = n_rem;
+  }
+}
+
+// grid (segments, 2 * B * Hq): elements above / equal to the k-th key T
+__global__ __launch_bounds__(256) void vs_tk_count_kernel(VsParams P) {
+  const int seg = blockIdx.x, a = blockIdx.y;
+  const TkArray t = tk_array(P, a);
+  if (!t.vs || t.k <= 0) return;
+  const int32_t* st = reinterpret_cast<const int32_t*>(P.ws_base + P.ws.tk_state) + 4 * a;
+  int32_t* cnt = reinterpret_cast<int32_t*>(P.ws_base + P.ws.tk_cnt) + 2 * ((size_t)a * P.ws.tk_segs + seg);
+  const uint32_t T = (uint32_t)st[0];
+  const int lo = seg * kTopkSeg, hi = min(lo + kTopkSeg, P.n);
+  constexpr int E = kTopkSeg / 256;
+  float x[E];
+  #pragma unroll
+  for (int e = 0; e < E; ++e) {
+    const int i = lo + threadIdx.x + 256 * e;
+    x[e] = i < hi ? t.src[i] : 0.f;
+  }
+  int gt = 0, eq = 0;
+  #pragma unroll
+  for (int e = 0; e < E; ++e) {
+    if (lo + threadIdx.x + 256 * e < hi) {
+      const uint32_t key = order_key(x[e]);
+      gt += key > T;
+      eq += key == T;
+    }
+  }
+  for (int off = 32; off > 0; off >>= 1) { gt += __shfl_xor(gt, off); eq += __shfl_xor(eq, off); }
+  __shared__ int pg[4], pe[4];
+  if ((threadIdx.x & 63) == 0) { pg[threadIdx.x >> 6] = gt; pe[threadIdx.x >> 6] = eq; }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    cnt[0] = pg[0] + pg[1] + pg[2] + pg[3];
+    cnt[1] = pe[0] + pe[1] + pe[2] + pe[3];
+  }
+}
+
+// grid (segments, 2 * B * Hq): ordered compaction of each segment; segment
+// s writes after the selections of segments < s, and takes the elements
+// equal to T that the earlier segments left of the quota.
+__global__ __launch_bounds__(256) void vs_tk_write_kernel(VsParams P) {
+  const int seg = blockIdx.x, a = blockIdx.y;
+  const TkArray t = tk_array(P, a);
+  if (!t.vs) return;
+  const int tid = threadIdx.x;
+  if (t.k <= 0) {
+    if (seg == 0)
+      for (int i = tid; i < t.cap; i += 256) t.out[i] = -1;
+    return;
+  }
+  const int32_t* st = reinterpret_cast<const int32_t*>(P.ws_base + P.ws.tk_state) + 4 * a;
+  const int32_t* cnt = reinterpret_cast<const int32_t*>(P.ws_base + P.ws.tk_cnt) + 2 * (size_t)a * P.ws.tk_segs;
+  const uint32_t T = (uint32_t)st[0];
+  const int need_eq = st[2];
+  __shared__ int base_out, eq_before;
+  __shared__ int scan[17];
+  if (tid == 0) {
+    int bo = 0, eb = 0;
+    for (int s2 = 0; s2 < seg; ++s2) {
+      const int g = cnt[2 * s2], e = cnt[2 * s2 + 1];
+      bo += g + max(0, min(e, need_eq - eb));
+      eb += e;
+    }
+    base_out = bo;
+    eq_before = eb;
+  }
+  __syncthreads();
+  constexpr int E = kTopkSeg / 256;        // consecutive elements per thread
+  const int lo = seg * kTopkSeg + tid * E;
+  float x[E];
+  #pragma unroll
+  for (int e = 0; e < E; ++e) x[e] = lo + e < P.n ? t.src[lo + e] : 0.f;
+  uint32_t key[E];
+  int n_gt = 0, n_eq = 0;
+  #pragma unroll
+  for (int e = 0; e < E; ++e) {
+    key[e] = order_key(x[e]);
+    if (lo + e < P.n) { n_gt += key[e] > T; n_eq += key[e] == T; }
+  }
+  int tot;
+  const int eq_rank0 = eq_before + block_scan_excl<256>(n_eq, scan, &tot);
+  const int take_eq = max(0, min(n_eq, need_eq - eq_rank0));
+  int pos = base_out + block_scan_excl<256>(n_gt + take_eq, scan, &tot);
+  int eq_seen = 0;
+  #pragma unroll
+  for (int e = 0; e < E; ++e) {
+    if (lo + e < P.n) {
+      bool sel = key[e] > T;
+      if (!sel && key[e] == T) { sel = eq_seen < take_eq; ++eq_seen; }
+      if (sel) t.out[pos++] = lo + e;
+    }
+  }
+  if (seg == 0)
+    for (int i = t.k + tid; i < t.cap; i += 256) t.out[i] = -1;
 }
 
 template <typename T, int DH>
@@ -340,7 +524,14 @@ hipError_t launch_t(const VsParams& p, hipStream_t st) {
   hipLaunchKernelGGL(vs_lse_kernel, dim3(16, BH), dim3(256), 0, st, p, (int)(nwg * 4));
   hipLaunchKernelGGL((vs_proxy_kernel<T, DH, 2>), dim3(nwg, BH), dim3(256), 0, st, p);
   hipLaunchKernelGGL(vs_diag_kernel, dim3((p.n + 255) / 256, BH), dim3(256), 0, st, p);
-  hipLaunchKernelGGL(vs_topk_kernel, dim3(2 * BH), dim3(1024), 0, st, p);
+  const dim3 tkg((unsigned)p.ws.tk_segs, 2 * BH);
+  hipLaunchKernelGGL(vs_tk_init_kernel, dim3(2 * BH), dim3(64), 0, st, p);
+  for (int shift = 24; shift >= 0; shift -= 8) {
+    hipLaunchKernelGGL(vs_tk_pass_kernel, tkg, dim3(256), 0, st, p, shift);
+    hipLaunchKernelGGL(vs_tk_pick_kernel, dim3(2 * BH), dim3(256), 0, st, p, shift);
+  }
+  hipLaunchKernelGGL(vs_tk_count_kernel, tkg, dim3(256), 0, st, p);
+  hipLaunchKernelGGL(vs_tk_write_kernel, tkg, dim3(256), 0, st, p);
   return hipGetLastError();
 }
 
