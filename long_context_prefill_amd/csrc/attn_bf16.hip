@@ -324,47 +324,41 @@ namespace {
 // once.  Inline assembly keeps the compiler from treating later LDS reads as
 // dependent on the copies (it would wait for the next chunk's copies before
 // reading the current slot); completion is waited for explicitly before the
-// barrier of each chunk.  M0 is restored afterwards; one wait state separates
+// barrier of each chunk.  M0 is declared clobbered; one wait state separates
 // the M0 write from the first copy.
 __device__ __forceinline__ void copy_chunk(const char* base, const uint32_t (&voff)[4], uint32_t dst) {
-  uint32_t keep;
   asm volatile(
-      "s_mov_b32 %0, m0\n\t"
-      "s_mov_b32 m0, %6\n\t"
+      "s_mov_b32 m0, %5\n\t"
       "s_nop 0\n\t"
-      "global_load_lds_dwordx4 %1, %5\n\t"
-      "global_load_lds_dwordx4 %2, %5 offset:1024\n\t"
-      "global_load_lds_dwordx4 %3, %5 offset:2048\n\t"
-      "global_load_lds_dwordx4 %4, %5 offset:3072\n\t"
-      "s_mov_b32 m0, %0"
-      : "=&s"(keep)
+      "global_load_lds_dwordx4 %0, %4\n\t"
+      "global_load_lds_dwordx4 %1, %4 offset:1024\n\t"
+      "global_load_lds_dwordx4 %2, %4 offset:2048\n\t"
+      "global_load_lds_dwordx4 %3, %4 offset:3072"
+      :
       : "v"(voff[0]), "v"(voff[1]), "v"(voff[2]), "v"(voff[3]), "s"(base), "s"(dst)
-      : "memory");
+      : "memory", "m0");
 }
 
 // The same copies with per-lane offsets that are not affine in i: one M0
 // write per copy and no instruction offset, so every voff[i] is the full,
 // non-negative byte offset of the lane's row piece from base.
 __device__ __forceinline__ void copy_rows(const char* base, const uint32_t (&voff)[4], uint32_t dst) {
-  uint32_t keep;
   asm volatile(
-      "s_mov_b32 %0, m0\n\t"
-      "s_mov_b32 m0, %6\n\t"
+      "s_mov_b32 m0, %5\n\t"
       "s_nop 0\n\t"
-      "global_load_lds_dwordx4 %1, %5\n\t"
-      "s_add_u32 m0, %6, 0x400\n\t"
+      "global_load_lds_dwordx4 %0, %4\n\t"
+      "s_add_u32 m0, %5, 0x400\n\t"
       "s_nop 0\n\t"
-      "global_load_lds_dwordx4 %2, %5\n\t"
-      "s_add_u32 m0, %6, 0x800\n\t"
+      "global_load_lds_dwordx4 %1, %4\n\t"
+      "s_add_u32 m0, %5, 0x800\n\t"
       "s_nop 0\n\t"
-      "global_load_lds_dwordx4 %3, %5\n\t"
-      "s_add_u32 m0, %6, 0xc00\n\t"
+      "global_load_lds_dwordx4 %2, %4\n\t"
+      "s_add_u32 m0, %5, 0xc00\n\t"
       "s_nop 0\n\t"
-      "global_load_lds_dwordx4 %4, %5\n\t"
-      "s_mov_b32 m0, %0"
-      : "=&s"(keep)
+      "global_load_lds_dwordx4 %3, %4"
+      :
       : "v"(voff[0]), "v"(voff[1]), "v"(voff[2]), "v"(voff[3]), "s"(base), "s"(dst)
-      : "memory", "scc");
+      : "memory", "scc", "m0");
 }
 
 // This wave's copies have landed and its LDS reads have returned; after the
@@ -441,7 +435,9 @@ __device__ __forceinline__ void attn_item(const AttnParams& P, const int b, cons
   // (w), the window limit of each row.  kNone may be conservative (unset
   // although nothing is kept); the per-element test is then exact.
   auto cflags = [&](int kstart, int vlo, int vhi, bool w) {
-    int f = (kstart >= 0 && kstart + 31 < n) ? kFast : 0;
+    // kFast iff 0 <= kstart <= n - 32 (both signs clear), kept in integer
+    // arithmetic so that it stays on the scalar unit
+    int f = ((kstart | (n - 32 - kstart)) >> 31) + 1;
     const int lo = w ? max(vlo, rw0 - win + 1) : vlo;
     if (lo > min(vhi, rlast)) return f | kNone;
     if (vlo > kstart || vhi < kstart + 31 || kstart + 31 > rw0 || (w && kstart < rlast - win + 1)) f |= kMask;
@@ -509,13 +505,17 @@ __device__ __forceinline__ void attn_item(const AttnParams& P, const int b, cons
       copy_chunk(src + (size_t)d.kstart * kRowB, is_v ? voff : koff, dst);
     } else {
       // per-lane rows: clamped into [0, n) (the excess keys are masked) or
-      // gathered from the column list; all keys are read before any copy
+      // gathered from the column list; all keys are read before any copy.
+      // (ks passes through an empty asm statement so that the per-lane
+      // arithmetic is not hoisted above the branch onto the fast path)
+      int ks = d.kstart;
+      asm volatile("" : "+s"(ks));
       uint32_t o[4];
       #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int r = crow0 + 4 * i;
-        int key = d.kstart + r;
-        if (d.flags & kGather) key = r < d.vhi ? L.colrow[d.kstart + r] : 0;
+        int key = ks + r;
+        if (d.flags & kGather) key = r < d.vhi ? L.colrow[ks + r] : 0;
         const uint32_t rb = (uint32_t)min(max(key, 0), n - 1) * kRowB;
         o[i] = rb + 16 * (cpiece ^ (is_v ? 4 * (r & 3) : (r & 15)));
       }
@@ -607,6 +607,11 @@ __device__ __forceinline__ void attn_item(const AttnParams& P, const int b, cons
     for (int i = 0; i < 16; ++i) acc[mb][i] = 0.f;
   float m_run = kMInit, l_run = 0.f;
   const float cfac = P.c;
+  // the rescale test compares raw scores against (m_run + tau) / c, so a
+  // chunk needs no multiply or add for it (c > 0); the threshold changes only
+  // with m_run
+  const float inv_c = 1.0f / cfac;
+  float thr = (m_run + kTau) * inv_c;
 
   typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
   const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
@@ -698,20 +703,23 @@ __device__ __forceinline__ void attn_item(const AttnParams& P, const int b, cons
     }
     apply_mask(s_cur, d0, bits0);
 
-    // online softmax of chunk j with lazy rescaling
-    float mx = fmaxf(fmaxf(fmaxf(s_cur[0], s_cur[1]), fmaxf(s_cur[2], s_cur[3])),
-                     fmaxf(fmaxf(s_cur[4], s_cur[5]), fmaxf(s_cur[6], s_cur[7])));
-    mx = fmaxf(mx, fmaxf(fmaxf(fmaxf(s_cur[8], s_cur[9]), fmaxf(s_cur[10], s_cur[11])),
-                         fmaxf(fmaxf(s_cur[12], s_cur[13]), fmaxf(s_cur[14], s_cur[15]))));
-    mx *= cfac;
-    if (__builtin_amdgcn_ballot_w64(mx > m_run + kTau)) {
-      const float pm = fmaxf(mx, __shfl_xor(mx, 32));      // the row's other 16 keys
+    // online softmax of chunk j with lazy rescaling; the lane's maximum in
+    // a tree of three-input maxima
+    auto max3 = [](float a, float b, float c) { return fmaxf(fmaxf(a, b), c); };
+    const float mx = fmaxf(max3(max3(s_cur[0], s_cur[1], s_cur[2]), max3(s_cur[3], s_cur[4], s_cur[5]),
+                                max3(s_cur[6], s_cur[7], s_cur[8])),
+                           max3(max3(s_cur[9], s_cur[10], s_cur[11]), max3(s_cur[12], s_cur[13], s_cur[14]),
+                                s_cur[15]));
+    if (__builtin_amdgcn_ballot_w64(mx > thr)) {
+      const float mxs = mx * cfac;
+      const float pm = fmaxf(mxs, __shfl_xor(mxs, 32));      // the row's other 16 keys
       const float mn = pm > m_run + kTau ? pm : m_run;
       const float alpha = fast_exp2(m_run - mn);
       #pragma unroll
       for (int mb = 0; mb < 4; ++mb) acc[mb] *= alpha;
       l_run *= alpha;
       m_run = mn;
+      thr = (m_run + kTau) * inv_c;
     }
     // Q.K of chunk j+1 (8 products) interleaved with the exponentials,
     // conversions and row sums of chunk j (48 vector instructions)
