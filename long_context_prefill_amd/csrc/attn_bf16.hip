@@ -443,8 +443,26 @@ __device__ __forceinline__ void attn_item(const AttnParams& P, const int b, cons
     if (vlo > kstart || vhi < kstart + 31 || kstart + 31 > rw0 || (w && kstart < rlast - win + 1)) f |= kMask;
     return f;
   };
-  // Chunk k of this item (wave-uniform).
-  auto describe = [&](int k) {
+  // Chunk k of this item (wave-uniform), in two steps: fetch reads the list
+  // entries it needs with scalar loads (a span's two offsets, a gathered
+  // chunk's first and last column, a selected block), decode derives the
+  // chunk from them.  In the steady loop the entries are fetched one
+  // iteration before they are decoded, so the loads are never waited for.
+  struct Raw { int a, b; };
+  auto fetch = [&](int k) {
+    Raw r{0, 0};
+    if constexpr (KIND == MINF_VSLASH) {
+      const bool span = k < Ca;
+      const int e = 32 * (k - Ca);
+      const int cnt = min(32, ncols - e);
+      r.a = ld_uniform(span ? L.clo : L.colrow, span ? k : e);
+      r.b = ld_uniform(span ? L.chi : L.colrow, span ? k : e + cnt - 1);
+    } else if constexpr (KIND == MINF_BSPARSE) {
+      r.a = ld_uniform(L.blkrow, k >> 1);
+    }
+    return r;
+  };
+  auto decode = [&](int k, const Raw& r) {
     Chunk d;
     if constexpr (KIND == MINF_ASHAPE) {
       const bool w = k >= Ca;
@@ -454,7 +472,7 @@ __device__ __forceinline__ void attn_item(const AttnParams& P, const int b, cons
       d.flags = cflags(d.kstart, d.vlo, d.vhi, w) | (w ? kWin : 0);
     } else if constexpr (KIND == MINF_VSLASH) {
       if (k < Ca) {
-        const int lo = ld_uniform(L.clo, k), hi = ld_uniform(L.chi, k);
+        const int lo = r.a, hi = r.b;
         d.kstart = row0 - hi;
         d.vlo = max(0, d.kstart);
         d.vhi = min(row0 - lo, n - 1);
@@ -463,14 +481,14 @@ __device__ __forceinline__ void attn_item(const AttnParams& P, const int b, cons
       } else {
         const int e = 32 * (k - Ca);
         const int cnt = min(32, ncols - e);
-        const int gfirst = ld_uniform(L.colrow, e), glast = ld_uniform(L.colrow, e + cnt - 1);
+        const int gfirst = r.a, glast = r.b;
         d.kstart = e;
         d.vlo = 0;
         d.vhi = cnt;
         d.flags = kGather | (gfirst > rlast ? kNone : 0) | ((cnt < 32 || glast > rw0) ? kMask : 0);
       }
     } else {
-      const int vb = ld_uniform(L.blkrow, k >> 1);
+      const int vb = r.a;
       if (vb < 0 || vb > u) {   // not a causal block: keep nothing
         d.kstart = 0; d.vlo = 1; d.vhi = 0; d.flags = kNone;
       } else {
@@ -482,6 +500,7 @@ __device__ __forceinline__ void attn_item(const AttnParams& P, const int b, cons
     }
     return d;
   };
+  auto describe = [&](int k) { return decode(k, fetch(k)); };
 
   // ---- copy offsets.  Wave w copies rows 16w + 4i + lane/16 (i = 0..3) of
   //      each tile; lane l writes LDS piece l%16 of its row, which holds the
@@ -656,10 +675,11 @@ __device__ __forceinline__ void attn_item(const AttnParams& P, const int b, cons
   //   (3.4% faster than ascending at 512K).
   const int step = KIND == MINF_BSPARSE ? -1 : 1;
   int kc = KIND == MINF_ASHAPE ? (2 * (slot & 127)) % C : (KIND == MINF_BSPARSE ? C - 1 : 0);
-  auto advance = [&]() {
-    kc += step;
-    kc = kc == C ? 0 : (kc < 0 ? C - 1 : kc);
+  auto next_of = [&](int k) {
+    k += step;
+    return k == C ? 0 : (k < 0 ? C - 1 : k);
   };
+  auto advance = [&]() { kc = next_of(kc); };
 
   // ---- software pipeline.  Chunk j lives in slot j%2 (K and V halves).  In
   //      iteration j the wave computes the softmax and P.V of chunk j and,
@@ -675,6 +695,10 @@ __device__ __forceinline__ void attn_item(const AttnParams& P, const int b, cons
     d1 = describe(kc);
     issue(d1, 1, false);
   }
+  // entries of the next chunk to decode (chunk 2), fetched ahead
+  constexpr bool kPrefetch = KIND != MINF_ASHAPE;
+  Raw rn{0, 0};
+  if (kPrefetch && C > 2) rn = fetch(next_of(kc));
   wait_copies_and_barrier();
   uint32_t bits0 = keep_bits(d0);
   floatx16 s_cur;
@@ -686,21 +710,34 @@ __device__ __forceinline__ void attn_item(const AttnParams& P, const int b, cons
   // iteration 0 rewrites the K half of slot 0, which both waves just read
   wait_copies_and_barrier();
 
-  // STEADY: chunks j+1 and j+2 exist (no bound tests)
+  // STEADY: chunks j+1 .. j+3 exist (j+1 .. j+2 for A-shape; no bound tests)
   auto iteration = [&](const int j, const int sl, auto steady) {
     constexpr bool STEADY = decltype(steady)::value;
-    // slot sl holds K and V of chunk j, slot sl^1 holds K of chunk j+1
+    // slot sl holds K and V of chunk j, slot sl^1 holds K of chunk j+1.
+    // Kinds with list entries decode chunk j+2 from the entries fetched
+    // during the previous iteration (already waited for before its barrier)
+    // and fetch those of chunk j+3; A-shape chunks are pure arithmetic.
     u32x4 kop[8], vop[2][4];
     const bool more = STEADY || j + 1 < C;
+    const bool more2 = STEADY || j + 2 < C;
     read_k(sl ^ 1, kop);
+    if constexpr (kPrefetch) {
+      if (more2) {
+        advance();
+        d2 = decode(kc, rn);
+        if (STEADY || j + 3 < C) rn = fetch(next_of(kc));
+      }
+    }
     uint32_t bits1 = 0u;
     if (more) bits1 = keep_bits(d1);
     if (more) issue(d1, sl ^ 1, true);
-    if (STEADY || j + 2 < C) {
-      advance();
-      d2 = describe(kc);
-      issue(d2, sl, false);
+    if constexpr (!kPrefetch) {
+      if (more2) {
+        advance();
+        d2 = describe(kc);
+      }
     }
+    if (more2) issue(d2, sl, false);
     apply_mask(s_cur, d0, bits0);
 
     // online softmax of chunk j with lazy rescaling; the lane's maximum in
@@ -764,7 +801,7 @@ __device__ __forceinline__ void attn_item(const AttnParams& P, const int b, cons
   };
 
   int j = 0;
-  for (; j + 3 < C; j += 2) {
+  for (; j + (kPrefetch ? 4 : 3) < C; j += 2) {
     iteration(j, 0, std::true_type{});
     wait_copies_and_barrier();
     iteration(j + 1, 1, std::true_type{});
