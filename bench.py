@@ -36,9 +36,9 @@ PEAK_HBM_GBS = 8000.0            # MI355X HBM3E
 ATTN_KERNEL = "attn_bf16_d128_kernel"
 ATTN_SOURCES = ["long_context_prefill_amd/csrc/attn_bf16.hip", "long_context_prefill_amd/csrc/common.h",
                 "long_context_prefill_amd/csrc/kernels.h", "include/minf.h"]
-ATTN_TRAFFIC = {"workload": "n128k_h32kv8_d128_bf16_mixed", "sources": "9f0031dd715b8310",
-                "fetch_kib": 19835308.54, "fetch_factor": 1048576 / 524304.85,
-                "write_kib": 2109351.72, "write_factor": 1048576 / 1048576.0}
+ATTN_TRAFFIC = {"workload": "n128k_h32kv8_d128_bf16_mixed", "sources": "28e3785b4fe3bb3a",
+                "fetch_kib": 20853949.08, "fetch_factor": 1048576 / 524304.54,
+                "write_kib": 2108084.08, "write_factor": 1048576 / 1048576.0}
 
 
 def log(*a):
