@@ -8,8 +8,8 @@
 // budget slots.  Everything is fp32 and free of floating-point atomics.
 //
 // GPU plan: a pooling pass streams Q (BS heads) and K (their KV heads) once
-// from HBM; a tiled fp32 product writes the causal score tiles of a batch of
-// heads into the workspace (so the score matrix never has to be resident for
+// from HBM; a tiled fp32 product on the matrix cores writes the causal score
+// tiles of a batch of heads into the workspace (so the score matrix never has to be resident for
 // the whole layer); one work-group per (head, query block) then runs the
 // exact radix top-k on its row.
 #include "kernels.h"
@@ -18,6 +18,8 @@
 namespace minf {
 
 namespace {
+
+typedef float floatx16 __attribute__((ext_vector_type(16)));
 
 struct BsBatch {
   int32_t count;
@@ -82,50 +84,71 @@ __global__ __launch_bounds__(256) void bs_pool_kernel(BsParams P, uint64_t kv_us
   }
 }
 
-// grid (tiles_v, tiles_u, batch): 64x64 causal tiles of R = scale * Qbar Kbar^T.
+// grid (tiles_v, tiles_u, batch): 128x128 causal tiles of R = scale * Qbar Kbar^T
+// on the fp32 matrix cores (v_mfma_f32_32x32x2_f32).  Wave w computes the
+// 64x64 quarter (w / 2, w % 2) as 2x2 products of 32x32; the waves share
+// nothing, so a quarter wholly above the diagonal simply exits.  Operands come
+// straight from the pooled rows (they stay in L2): lane (m, hh) of a product
+// holds element k of row m, and the contraction index is permuted alike for
+// both operands, k = k0 + 4 hh + s at step s of the 8-wide slab k0, so one
+// 16-byte load per row and lane feeds four steps.
 template <int DH>
 __global__ __launch_bounds__(256) void bs_score_kernel(BsParams P, BsBatch batch) {
   const int tv = blockIdx.x, tu = blockIdx.y;
   if (tv > tu) return;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int m = lane & 31, hh = lane >> 5;
+  const int u0 = 128 * tu + 64 * (wave >> 1), v0 = 128 * tv + 64 * (wave & 1);
+  if (v0 > u0 + 63 || u0 >= P.nq) return;
   const int bh = batch.bh[blockIdx.z];
   const int b = bh / P.Hq, h = bh % P.Hq;
   const int kv = h / (P.Hq / P.Hkv);
   const float* A = P.qbar + (size_t)bh * P.nq * DH;
   const float* Bm = P.kbar + ((size_t)b * P.Hkv + kv) * P.nq * DH;
   float* R = P.scores + (size_t)blockIdx.z * P.nq * P.nq;
-  __shared__ float sa[16][65], sb[16][65];
-  const int tx = threadIdx.x & 15, ty = threadIdx.x >> 4;
-  float acc[4][4] = {};
-  for (int k0 = 0; k0 < DH; k0 += 16) {
-    for (int i = threadIdx.x; i < 64 * 16; i += 256) {
-      const int r = i >> 4, kk = i & 15;
-      const int ua = 64 * tu + r, vb = 64 * tv + r;
-      sa[kk][r] = ua < P.nq ? A[(size_t)ua * DH + k0 + kk] : 0.f;
-      sb[kk][r] = vb < P.nq ? Bm[(size_t)vb * DH + k0 + kk] : 0.f;
-    }
-    __syncthreads();
-    #pragma unroll
-    for (int kk = 0; kk < 16; ++kk) {
-      float a[4], bv[4];
-      #pragma unroll
-      for (int i = 0; i < 4; ++i) { a[i] = sa[kk][ty + 16 * i]; bv[i] = sb[kk][tx + 16 * i]; }
-      #pragma unroll
-      for (int i = 0; i < 4; ++i)
-        #pragma unroll
-        for (int jx = 0; jx < 4; ++jx) acc[i][jx] = __builtin_fmaf(a[i], bv[jx], acc[i][jx]);
-    }
-    __syncthreads();
-  }
+  // rows past nq are clamped to the last row: computed, never stored
+  const float* pa[2];
+  const float* pb[2];
   #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int uu = 64 * tu + ty + 16 * i;
-    if (uu >= P.nq) continue;
-    #pragma unroll
-    for (int jx = 0; jx < 4; ++jx) {
-      const int vv = 64 * tv + tx + 16 * jx;
-      if (vv <= uu) R[(size_t)uu * P.nq + vv] = P.scale * acc[i][jx];
-    }
+  for (int i = 0; i < 2; ++i) {
+    pa[i] = A + (size_t)min(u0 + 32 * i + m, P.nq - 1) * DH + 4 * hh;
+    pb[i] = Bm + (size_t)min(v0 + 32 * i + m, P.nq - 1) * DH + 4 * hh;
   }
+  floatx16 acc[2][2];
+  #pragma unroll
+  for (int i = 0; i < 2; ++i)
+    #pragma unroll
+    for (int jx = 0; jx < 2; ++jx)
+      #pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][jx][r] = 0.f;
+  #pragma unroll 4
+  for (int k0 = 0; k0 < DH; k0 += 8) {
+    floatx4 xa[2], xb[2];
+    #pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      xa[i] = *reinterpret_cast<const floatx4*>(pa[i] + k0);
+      xb[i] = *reinterpret_cast<const floatx4*>(pb[i] + k0);
+    }
+    #pragma unroll
+    for (int st = 0; st < 4; ++st)
+      #pragma unroll
+      for (int i = 0; i < 2; ++i)
+        #pragma unroll
+        for (int jx = 0; jx < 2; ++jx)
+          acc[i][jx] = __builtin_amdgcn_mfma_f32_32x32x2f32(xa[i][st], xb[jx][st], acc[i][jx], 0, 0, 0);
+  }
+  // lane (m, hh), register r of a 32x32 product: row 8 (r / 4) + 4 hh + r % 4, column m
+  #pragma unroll
+  for (int i = 0; i < 2; ++i)
+    #pragma unroll
+    for (int jx = 0; jx < 2; ++jx) {
+      const int vv = v0 + 32 * jx + m;
+      #pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int uu = u0 + 32 * i + 8 * (r >> 2) + 4 * hh + (r & 3);
+        if (uu < P.nq && vv <= uu) R[(size_t)uu * P.nq + vv] = P.scale * acc[i][jx][r];
+      }
+    }
 }
 
 // grid (nq, batch): exact top-k of row u over v <= u, the row held in
@@ -162,7 +185,7 @@ hipError_t launch_t(const BsParams& p, hipStream_t st) {
     if (p.ht.kind[h] == MINF_BSPARSE) kv_used |= 1ull << (h / (p.Hq / p.Hkv));
   hipLaunchKernelGGL((bs_pool_kernel<T, DH>), dim3(p.nq, p.B * (p.Hq + p.Hkv)), dim3(256), 0, st, p, kv_used);
   BsBatch batch{};
-  const int tiles = (p.nq + 63) / 64;
+  const int tiles = (p.nq + 127) / 128;
   auto flush = [&]() {
     if (!batch.count) return;
     hipLaunchKernelGGL((bs_score_kernel<DH>), dim3(tiles, tiles, batch.count), dim3(256), 0, st, p, batch);
