@@ -213,6 +213,57 @@ def time_layer(M, prob, heads, Q, K, V, O_, steps, warmup, index=True, flush=Non
     return float(np.median(ms)), kept
 
 
+def pattern_search(a):
+    """The offline kernel-aware pattern search on a synthetic calibration layer
+    (KV groups with local, planted and clustered structure), B=1, Hq=32,
+    Hkv=8, dh=128, bf16, length a.search; one JSON line."""
+    import numpy as np
+    import torch
+    import long_context_prefill_amd as M
+    from long_context_prefill_amd import search as S
+    from synth import gen
+    n = a.search
+    t0 = time.time()
+    p = gen.make_calibration(n=n, Hq=32, Hkv=8, dh=128, dtype="bf16")
+    log(f"generated {p.name} in {time.time() - t0:.1f}s")
+    conv = lambda x: torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).cuda()
+    prob = M.make_problem(1, 32, 8, n, 128, "bf16", "f32")
+    t0 = time.time()
+    res = S.search(prob, conv(p.Q), conv(p.K), conv(p.V), eps=a.search_eps, reps=max(1, a.steps))
+    log(f"search in {time.time() - t0:.1f}s")
+    kinds = {}
+    for c in res["table_cfgs"]:
+        k = ("ashape", "vslash", "bsparse")[c[0]]
+        kinds[k] = kinds.get(k, 0) + 1
+    by_group = {}
+    for h, ch in enumerate(res["choice"]):
+        g = p.meta["group_kinds"][h // 4]
+        by_group.setdefault(g, []).append(res["candidates"][ch])
+    out = {
+        "metric": "offline pattern search: layer ms of the chosen per-head table vs dense, error <= eps",
+        "config": {"workload": p.name, "B": 1, "n": n, "Hq": 32, "Hkv": 8, "dh": 128,
+                   "structure_by_kv_group": p.meta["group_kinds"]},
+        "data": "synthetic calibration layer, seeded",
+        "eps": res["eps"],
+        "candidates": res["candidates"],
+        "times_ms": [round(t, 4) for t in res["times_ms"]],
+        "dense_ms": round(res["dense_ms"], 4),
+        "table_ms": round(res["table_ms"], 4),
+        "speedup_vs_dense": round(res["dense_ms"] / res["table_ms"], 3),
+        "table_kinds": kinds,
+        "choice_by_structure": by_group,
+        "measure": res["measure"],
+        "max_table_missed_mass": round(max(res["table_missed_mass"]), 5),
+        "max_table_rel_err": round(max(res["table_rel_err"]), 5),
+        "best_missed_mass_by_structure": {
+            g: [round(min(res["missed_mass"][h][c] for h in range(32) if p.meta["group_kinds"][h // 4] == g), 4)
+                for c in range(len(res["candidates"]))]
+            for g in sorted(set(p.meta["group_kinds"]))},
+        "timing": "median of the timed runs after one warm-up run, warm caches; each candidate on all heads",
+    }
+    print(json.dumps(out), flush=True)
+
+
 def crossover(a):
     """Sparse layer (index + attention, the 128K mixed pattern table) against
     the dense causal baseline over sequence lengths, on planted inputs of
@@ -262,6 +313,9 @@ def main():
                     help="comma-separated lengths: time the sparse layer against the dense causal baseline")
     ap.add_argument("--no-dense", action="store_true", help="skip the dense causal baseline")
     ap.add_argument("--no-exact", action="store_true", help="skip the exact slash pairs (slash_tile=1) layer")
+    ap.add_argument("--search", type=int, default=0,
+                    help="only run the offline pattern search on a calibration layer of this length")
+    ap.add_argument("--search-eps", type=float, default=0.05, help="output-error bound of the pattern search")
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="only run a plain device copy of this many MiB (memory-counter calibration)")
     a = ap.parse_args()
@@ -275,6 +329,9 @@ def main():
         return
     if a.crossover:
         crossover(a)
+        return
+    if a.search:
+        pattern_search(a)
         return
 
     import numpy as np

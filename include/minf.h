@@ -229,6 +229,33 @@ minf_status minf_sparse_attn(const minf_problem* prob, const minf_head_cfg* head
                              void* O, float* lse,
                              void* ws, size_t ws_bytes, void* stream);
 
+/* Per-head output error, for the offline kernel-aware pattern search
+ * (MInference page sections 3.1 and 6.3; blog section 2.3.1, Eq. 2: each
+ * candidate pattern's attention is compared with dense attention on a
+ * calibration input).  For every (b, h), with O and O_ref [B, Hq, n, dh] in
+ * the problem's out_dtype (device memory, read only):
+ *   err[2 (b Hq + h)]     = sum over rows and columns of (O - O_ref)^2,
+ *   err[2 (b Hq + h) + 1] = sum of O_ref^2,
+ * accumulated in fp64 in a fixed order (two runs give identical bits).
+ * err: device memory of 2 B Hq doubles, written.  Only B, Hq, n, dh and
+ * out_dtype of *prob are read; the head table is not needed.  MINF_EINVAL
+ * for null pointers or bad sizes, MINF_EUNSUPPORTED for dh not 64 or 128. */
+minf_status minf_output_error(const minf_problem* prob, const void* O, const void* O_ref, double* err, void* stream);
+
+/* Captured attention mass, for the same search (MInference page section
+ * 3.1, "covered attention mass"; blog section 2.3.1, Eq. 2): a row whose
+ * kept keys carry the fraction m of the dense softmax has
+ * m = exp(lse - lse_ref), with lse from minf_sparse_attn for the candidate
+ * and lse_ref for dense attention, and Eq. 2's L1 distance between the
+ * renormalised and the dense attention row is 2 (1 - m).  For every (b, h):
+ *   mass[b Hq + h] = sum over the n rows of exp(lse - lse_ref)
+ * (rows with lse = -inf, i.e. no kept key, add 0), fp64, fixed order.
+ * lse, lse_ref: device [B, Hq, n] fp32, read only; mass: device, B Hq
+ * doubles, written.  Only B, Hq and n of *prob are read.  MINF_EINVAL for
+ * null pointers or bad sizes. */
+minf_status minf_captured_mass(const minf_problem* prob, const float* lse, const float* lse_ref, double* mass,
+                               void* stream);
+
 /* Kernel timing, for measurement harnesses; computing never needs it.
  * After minf_timing_start(max_calls), each of the next max_calls calls of
  * minf_sparse_attn records a HIP event pair on its stream around its main

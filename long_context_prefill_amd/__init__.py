@@ -12,6 +12,10 @@ Entry points (same names and argument order as include/minf.h):
     minf_bs_index(prob, heads, Q, K, blk_idx, blk_cnt, ws, stream=None)
     minf_build_tiles(prob, heads, vert_idx, slash_idx, blk_idx, blk_cnt, tiles, ws, stream=None)
     minf_sparse_attn(prob, heads, Q, K, V, blk_idx, blk_cnt, tiles, O, lse, ws, stream=None)
+    minf_output_error(prob, O, O_ref, err, stream=None)
+    minf_captured_mass(prob, lse, lse_ref, mass, stream=None)
+The offline pattern search that drives them on calibration input is in
+long_context_prefill_amd.search.
 """
 from __future__ import annotations
 
@@ -29,8 +33,8 @@ MINF_FORCE_FIRST_BLOCK, MINF_FORCE_DIAG_BLOCK = 1, 2
 MINF_DEV_BAD_VERTICAL, MINF_DEV_BAD_SLASH, MINF_DEV_BAD_BLOCK, MINF_DEV_CAPACITY = 1, 2, 4, 8
 
 EXPORTED = ["minf_query_sizes", "minf_vs_index", "minf_bs_index", "minf_build_tiles",
-            "minf_sparse_attn", "minf_timing_start", "minf_timing_read", "minf_status_string",
-            "minf_last_error", "minf_version"]
+            "minf_sparse_attn", "minf_output_error", "minf_captured_mass", "minf_timing_start",
+            "minf_timing_read", "minf_status_string", "minf_last_error", "minf_version"]
 
 
 class MinfError(RuntimeError):
@@ -85,7 +89,10 @@ def load_library(path: str = LIB_PATH):
                                      ctypes.c_size_t, vp]
     lib.minf_sparse_attn.argtypes = [P(MinfProblem), P(MinfHeadCfg), vp, vp, vp, vp, vp, P(MinfTiles), vp, vp,
                                      vp, ctypes.c_size_t, vp]
-    for f in ("minf_query_sizes", "minf_vs_index", "minf_bs_index", "minf_build_tiles", "minf_sparse_attn"):
+    lib.minf_output_error.argtypes = [P(MinfProblem), vp, vp, vp, vp]
+    lib.minf_captured_mass.argtypes = [P(MinfProblem), vp, vp, vp, vp]
+    for f in ("minf_query_sizes", "minf_vs_index", "minf_bs_index", "minf_build_tiles", "minf_sparse_attn",
+              "minf_output_error", "minf_captured_mass"):
         getattr(lib, f).restype = ctypes.c_int
     lib.minf_timing_start.argtypes = [ctypes.c_int32]
     lib.minf_timing_start.restype = ctypes.c_int
@@ -186,6 +193,20 @@ def minf_sparse_attn(prob, heads, Q, K, V, blk_idx, blk_cnt, tiles: Optional[dic
     _check(lib.minf_sparse_attn(ctypes.byref(prob), heads, _ptr(Q), _ptr(K), _ptr(V), _ptr(blk_idx),
                                 _ptr(blk_cnt), ctypes.byref(ts), _ptr(O), _ptr(lse), _ptr(ws), _nbytes(ws),
                                 _stream(stream)))
+
+
+def minf_output_error(prob, O, O_ref, err, stream=None):
+    """err (device, 2 * B * Hq float64) <- per head: sum of (O - O_ref)^2 and
+    sum of O_ref^2."""
+    lib = load_library()
+    _check(lib.minf_output_error(ctypes.byref(prob), _ptr(O), _ptr(O_ref), _ptr(err), _stream(stream)))
+
+
+def minf_captured_mass(prob, lse, lse_ref, mass, stream=None):
+    """mass (device, B * Hq float64) <- per head: sum over rows of
+    exp(lse - lse_ref)."""
+    lib = load_library()
+    _check(lib.minf_captured_mass(ctypes.byref(prob), _ptr(lse), _ptr(lse_ref), _ptr(mass), _stream(stream)))
 
 
 def minf_timing_start(max_calls: int):

@@ -360,6 +360,32 @@ minf_status minf_sparse_attn(const minf_problem* prob, const minf_head_cfg* head
                     "minf_sparse_attn launch");
 }
 
+minf_status minf_output_error(const minf_problem* prob, const void* O, const void* O_ref, double* err, void* stream) {
+  g_err[0] = 0;
+  if (!prob || !O || !O_ref || !err) return fail(MINF_EINVAL, "null problem, O, O_ref or err");
+  if (prob->B < 1 || prob->n < 1 || prob->Hq < 1 || prob->Hq > MINF_MAX_HEADS)
+    return fail(MINF_EINVAL, "B, n must be >= 1 and Hq in [1, %d] (B=%d n=%d Hq=%d)", MINF_MAX_HEADS, prob->B, prob->n,
+                prob->Hq);
+  if (prob->dh != 64 && prob->dh != 128) return fail(MINF_EUNSUPPORTED, "dh must be 64 or 128 (dh=%d)", prob->dh);
+  if (prob->out_dtype != MINF_F32 && prob->out_dtype != MINF_BF16)
+    return fail(MINF_EINVAL, "bad out_dtype %d", prob->out_dtype);
+  return hip_status(minf::launch_output_error(O, O_ref, (int64_t)prob->B * prob->Hq, (int64_t)prob->n * prob->dh,
+                                              prob->out_dtype == MINF_BF16, err, static_cast<hipStream_t>(stream)),
+                    "minf_output_error launch");
+}
+
+minf_status minf_captured_mass(const minf_problem* prob, const float* lse, const float* lse_ref, double* mass,
+                               void* stream) {
+  g_err[0] = 0;
+  if (!prob || !lse || !lse_ref || !mass) return fail(MINF_EINVAL, "null problem, lse, lse_ref or mass");
+  if (prob->B < 1 || prob->n < 1 || prob->Hq < 1 || prob->Hq > MINF_MAX_HEADS)
+    return fail(MINF_EINVAL, "B, n must be >= 1 and Hq in [1, %d] (B=%d n=%d Hq=%d)", MINF_MAX_HEADS, prob->B, prob->n,
+                prob->Hq);
+  return hip_status(minf::launch_captured_mass(lse, lse_ref, (int64_t)prob->B * prob->Hq, prob->n, mass,
+                                               static_cast<hipStream_t>(stream)),
+                    "minf_captured_mass launch");
+}
+
 minf_status minf_timing_start(int32_t max_calls) {
   if (max_calls < 1 || max_calls > 65536) return fail(MINF_EINVAL, "max_calls %d outside [1, 65536]", max_calls);
   timing_release();

@@ -24,7 +24,12 @@ Readings taken where the pages are open (each is listed in the design doc):
   ([MInf] section 2, Block-Sparse; [Blog] section 2.3.2);
 * top-k orders by (score descending, index ascending) and returns the chosen
   indices sorted ascending;
-* an empty candidate row gives o = 0 and LSE = -inf.
+* an empty candidate row gives o = 0 and LSE = -inf;
+* the pattern search ([MInf] sections 3.1 and 6.3; [Blog] section 2.3.1)
+  measures a candidate by its missed attention mass 1 - m (m the row mean of
+  the dense softmax mass its kept keys carry; Eq. 2's L1 row distance is
+  2 (1 - m)) or by its relative output error, and keeps per head the least
+  time among candidates within the bound, ties to the earlier candidate.
 
 Parity status: every function below is pinned by tests/test_oracle_*.py
 against values printed on the pages, closed forms, invariants, special cases
@@ -504,3 +509,79 @@ def run_layer(Q, K, V, dtype: str, heads, scale: float = 0.0, rows=None, slash_t
         for bh in items:
             out[bh] = one(bh)[1]
     return {"heads": out, "O": O, "LSE": LSE, "rows": rows, "scale": sc}
+
+
+# ----------------------------------------------------------------------------
+# offline pattern search ([MInf] sections 3.1 and 6.3; [Blog] section 2.3.1,
+# Eq. 2: each candidate's attention is compared with dense attention on a
+# calibration input, and among acceptable candidates the faster is kept)
+# ----------------------------------------------------------------------------
+
+def output_error(O, O_ref):
+    """Per head of [B, H, R, dh] outputs: (sum over batch, rows and columns of
+    (O - O_ref)^2, sum of O_ref^2), both float64 arrays of length H."""
+    a = np.asarray(O, dtype=np.float64)
+    r = np.asarray(O_ref, dtype=np.float64)
+    d = a - r
+    return (d * d).sum(axis=(0, 2, 3)), (r * r).sum(axis=(0, 2, 3))
+
+
+def relative_output_error(O, O_ref) -> np.ndarray:
+    """||O_h - O_ref,h||_F / ||O_ref,h||_F per head (0 where both are 0)."""
+    d2, r2 = output_error(O, O_ref)
+    out = np.empty_like(d2)
+    for h in range(d2.shape[0]):
+        if r2[h] > 0:
+            out[h] = math.sqrt(d2[h] / r2[h])
+        else:
+            out[h] = 0.0 if d2[h] == 0 else math.inf
+    return out
+
+
+def choose_patterns(err, times, eps: float) -> List[int]:
+    """err [H, C] per-head errors of C candidates, times [C]: per head, the
+    candidate of least time among those with error <= eps, ties to the
+    lower candidate index; -1 where none qualifies."""
+    err = np.asarray(err, dtype=np.float64)
+    times = np.asarray(times, dtype=np.float64)
+    out = []
+    for h in range(err.shape[0]):
+        ok = np.flatnonzero(err[h] <= eps)
+        out.append(int(ok[np.argmin(times[ok])]) if ok.size else -1)
+    return out
+
+
+def captured_mass(q, k, rows: np.ndarray, mask_fn: Callable, scale: float, chunk: int = 64) -> np.ndarray:
+    """Per row i of rows: the fraction of the dense causal softmax of row i
+    (keys j <= i) that the keys kept by mask_fn carry ([MInf] section 3.1,
+    the covered attention mass), from the explicit probabilities."""
+    n = k.shape[0]
+    rows = np.asarray(rows, dtype=np.int64)
+    out = np.empty(rows.shape[0])
+    for s in range(0, rows.shape[0], chunk):
+        r = rows[s:s + chunk]
+        causal = np.arange(n)[None, :] <= r[:, None]
+        sc = np.where(causal, scale * (q[r] @ k.T), -np.inf)
+        p = np.exp(sc - sc.max(axis=1, keepdims=True))
+        p /= p.sum(axis=1, keepdims=True)
+        out[s:s + r.shape[0]] = (p * (mask_fn(r, n) & causal)).sum(axis=1)
+    return out
+
+
+def layer_missed_mass(Q, K, dtype: str, heads, scale: float = 0.0, rows=None, workers=None) -> np.ndarray:
+    """Per head h: 1 - the mean captured mass over the batch and the rows
+    (all rows if None) under the layer's index estimation."""
+    B, Hq, n, dh = Q.shape
+    Hkv = K.shape[1]
+    sc = scale if scale else 1.0 / math.sqrt(dh)
+    rows = np.arange(n, dtype=np.int64) if rows is None else np.asarray(rows, dtype=np.int64)
+    res = run_layer(Q, K, Q[:, :Hkv], dtype, heads, scale, rows=rows, attend=False, workers=workers)["heads"]
+    out = np.zeros(Hq)
+    for h in range(Hq):
+        tot = 0.0
+        for b in range(B):
+            q = widen(Q[b, h], dtype)
+            k = widen(K[b, kv_head(h, Hq, Hkv)], dtype)
+            tot += captured_mass(q, k, rows, res[(b, h)].mask_fn, sc).sum()
+        out[h] = 1.0 - tot / (B * rows.shape[0])
+    return out

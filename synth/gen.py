@@ -202,6 +202,41 @@ def _planted_tensor(seed_seq, n, dh, dirs_k, sinks, is_key, dtype,
     return out
 
 
+def _local_features(pos: np.ndarray, harmonics: int, lmin: float = 32.0, lmax: float = 4096.0) -> np.ndarray:
+    """[len(pos), 2H] matrix of cos, sin of 2 pi p / L_m for H wavelengths L_m
+    spaced geometrically from lmin to lmax: their dot product between
+    positions i and j is sum_m cos(2 pi (i - j) / L_m), largest at i = j."""
+    m = np.arange(harmonics, dtype=np.float64)
+    lam = lmin * (lmax / lmin) ** (m / max(harmonics - 1, 1))
+    ang = pos.astype(np.float64)[:, None] * (2.0 * math.pi / lam)[None, :]
+    f = np.empty((pos.shape[0], 2 * harmonics))
+    f[:, 0::2] = np.cos(ang)
+    f[:, 1::2] = np.sin(ang)
+    return f
+
+
+def _local_tensor(seed_seq, n, dh, dirs_k, n_sinks, is_key, dtype, harmonics, sink_amp, amp):
+    """Local structure: iid noise plus positional features that make q_i . k_j
+    peak near i = j, and the first n_sinks keys raised along a direction that
+    every query shares (the sink of an A-shape head)."""
+    rng = np.random.Generator(np.random.PCG64(seed_seq))
+    out = np.empty((n, dh), dtype=np.uint16 if dtype == "bf16" else np.float32)
+    step = 1 << 16
+    u = dirs_k[:, 0]
+    feat_dirs = dirs_k[:, 1:]
+    for s in range(0, n, step):
+        e = min(n, s + step)
+        x = rng.standard_normal((e - s, dh))
+        x += amp * (_local_features(np.arange(s, e), harmonics) @ feat_dirs.T)
+        if is_key:
+            if s < n_sinks:
+                x[:min(n_sinks, e) - s] += sink_amp * u[None, :]
+        else:
+            x += sink_amp * u[None, :]
+        out[s:e] = _round(x, dtype)
+    return out
+
+
 def _iid_tensor(seed_seq, n, dh, dtype):
     rng = np.random.Generator(np.random.PCG64(seed_seq))
     out = np.empty((n, dh), dtype=np.uint16 if dtype == "bf16" else np.float32)
@@ -236,6 +271,9 @@ def _cluster_runs(rng, n, n_clusters, lo=32, hi=512):
     return ids
 
 
+CALIB_KINDS = ("local", "planted", "clustered")
+
+
 def _sample_rows(rng, n, count=4096):
     if count >= n:
         return np.arange(n, dtype=np.int64)
@@ -253,7 +291,10 @@ def generate(name, B, Hq, Hkv, n, dh, dtype, heads, seed, dist="iid",
              n_clusters=256, cluster_sigma=0.5):
     """Draw one problem.
 
-    dist: "iid" (N(0,1)), "planted" (sinks + periodic comb) or "clustered".
+    dist: "iid" (N(0,1)), "planted" (sinks + periodic comb), "clustered", or
+          "calibration": KV group kv takes the structure CALIB_KINDS[kv % 3]
+          (local, planted or clustered), so that the heads of one layer want
+          different patterns.
     sample_rows: None to check every row, else the number of sampled rows.
     """
     assert Hq % Hkv == 0 and len(heads) == Hq
@@ -304,6 +345,44 @@ def generate(name, B, Hq, Hkv, n, dh, dtype, heads, seed, dist="iid",
             for kv in range(Hkv):
                 jobs.append((K, (b, kv), _clustered_tensor,
                              (k_seeds[b * Hkv + kv], centres[kv], ids, cluster_sigma, dtype)))
+                jobs.append((V, (b, kv), _iid_tensor, (v_seeds[b * Hkv + kv], n, dh, dtype)))
+    elif dist == "calibration":
+        sink_amp = math.sqrt(3.0 * math.sqrt(dh))
+        comb_amp = math.sqrt(3.0 * math.sqrt(dh) / harmonics)
+        # local: q_i . k_i / sqrt(dh) is about 24 from the positional
+        # features, against a spread of about 24 / sqrt(2 harmonics) far
+        # from the diagonal, so that little mass lies beyond a few thousand
+        # keys even at long lengths
+        local_amp = math.sqrt(24.0 * math.sqrt(dh) / harmonics)
+        kinds = [CALIB_KINDS[kv % 3] for kv in range(Hkv)]
+        meta.update(group_kinds=kinds, period=period, harmonics=harmonics)
+        for b in range(B):
+            sinks, dirs = _planted_structure(st, Hkv, n, dh, n_sinks, period, harmonics)
+            centres = [st.standard_normal((n_clusters, dh)) for _ in range(Hkv)]
+            ids = _cluster_runs(st, n, n_clusters)
+            for kv in range(Hkv):
+                kind = kinds[kv]
+                heads_kv = range(kv * g, (kv + 1) * g)
+                if kind == "local":
+                    for h in heads_kv:
+                        jobs.append((Q, (b, h), _local_tensor, (q_seeds[b * Hq + h], n, dh, dirs[kv], 4, False,
+                                                                 dtype, harmonics, sink_amp, local_amp)))
+                    jobs.append((K, (b, kv), _local_tensor, (k_seeds[b * Hkv + kv], n, dh, dirs[kv], 4, True,
+                                                              dtype, harmonics, sink_amp, local_amp)))
+                elif kind == "planted":
+                    for h in heads_kv:
+                        jobs.append((Q, (b, h), _planted_tensor,
+                                     (q_seeds[b * Hq + h], n, dh, dirs[kv], sinks, False,
+                                      dtype, period, harmonics, sink_amp, comb_amp)))
+                    jobs.append((K, (b, kv), _planted_tensor,
+                                 (k_seeds[b * Hkv + kv], n, dh, dirs[kv], sinks, True,
+                                  dtype, period, harmonics, sink_amp, comb_amp)))
+                else:
+                    for h in heads_kv:
+                        jobs.append((Q, (b, h), _clustered_tensor,
+                                     (q_seeds[b * Hq + h], centres[kv], ids, cluster_sigma, dtype)))
+                    jobs.append((K, (b, kv), _clustered_tensor,
+                                 (k_seeds[b * Hkv + kv], centres[kv], ids, cluster_sigma, dtype)))
                 jobs.append((V, (b, kv), _iid_tensor, (v_seeds[b * Hkv + kv], n, dh, dtype)))
     elif dist == "iid":
         for b in range(B):
@@ -398,3 +477,16 @@ def make_small(n=1000, B=1, Hq=8, Hkv=2, dh=128, dtype="bf16", heads=None,
         kw.setdefault("n_sinks", 4)
     return generate(f"small_n{n}_b{B}_h{Hq}kv{Hkv}_d{dh}_{dtype}", B, Hq, Hkv, n, dh, dtype,
                     heads, seed, dist=dist, scale=scale, workers=workers, **kw)
+
+
+def make_calibration(n=16384, B=1, Hq=32, Hkv=8, dh=128, dtype="bf16", seed=2024, period=1024, harmonics=16,
+                     n_sinks=16, n_clusters=16, workers=None) -> Problem:
+    """A calibration layer for the pattern search: KV groups cycle through
+    local, planted and clustered structure (CALIB_KINDS); few clusters, so
+    that a clustered head's keys recur in blocks across the whole sequence.
+    The pattern table it carries is a placeholder (every head dense); the
+    search replaces it."""
+    heads = [ashape(0, n)] * Hq
+    return generate(f"calib_n{n}_h{Hq}kv{Hkv}_d{dh}_{dtype}", B, Hq, Hkv, n, dh, dtype, heads, seed,
+                    dist="calibration", period=period, harmonics=harmonics, n_sinks=n_sinks,
+                    n_clusters=n_clusters, workers=workers)

@@ -145,3 +145,19 @@ def test_timing_rejects_bad_arguments(lib):
     assert lib.minf_timing_read(None, 0, ctypes.byref(cnt)) == M.MINF_EINVAL   # no timing started
     assert lib.minf_timing_read(None, 4, ctypes.byref(cnt)) == M.MINF_EINVAL   # null output array
     assert lib.minf_timing_read(None, 0, None) == M.MINF_EINVAL
+
+
+def test_output_error_rejects_bad_arguments(lib):
+    """minf_output_error validates before any launch (the fake pointers are
+    never dereferenced)."""
+    fake = 0x1000
+    p = _prob()
+    assert lib.minf_output_error(None, fake, fake, fake, None) == M.MINF_EINVAL
+    assert lib.minf_output_error(ctypes.byref(p), None, fake, fake, None) == M.MINF_EINVAL
+    assert lib.minf_output_error(ctypes.byref(p), fake, None, fake, None) == M.MINF_EINVAL
+    assert lib.minf_output_error(ctypes.byref(p), fake, fake, None, None) == M.MINF_EINVAL
+    p96 = _prob(dh=96)
+    assert lib.minf_output_error(ctypes.byref(p96), fake, fake, fake, None) == M.MINF_EUNSUPPORTED
+    p0 = _prob(n=0)
+    assert lib.minf_output_error(ctypes.byref(p0), fake, fake, fake, None) == M.MINF_EINVAL
+    assert lib.minf_last_error().decode()
