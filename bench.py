@@ -264,6 +264,87 @@ def pattern_search(a):
     print(json.dumps(out), flush=True)
 
 
+RAGGED_LENS = [65536, 8192, 32768, 4096, 16384, 49152, 12288, 24576]
+
+
+def ragged_batch(a):
+    """Eight prompts of 4K-64K tokens (planted inputs, the 128K layer's mixed
+    pattern table), packed without padding through minf_prefill_ragged,
+    against the same prompts padded to the longest as one B = 8 batch
+    through the four calls; one JSON line."""
+    import numpy as np
+    import torch
+    import long_context_prefill_amd as M
+    from synth import gen
+    Hq, Hkv, dh = 32, 8, 128
+    table = gen.pattern_table(3)
+    heads = M.make_heads(table)
+    lens = RAGGED_LENS
+    n_max, T = max(lens), sum(lens)
+    t0 = time.time()
+    samples = [gen.generate(f"req{i}_n{n}", 1, Hq, Hkv, n, dh, "bf16", table, 5000 + i, dist="planted")
+               for i, n in enumerate(lens)]
+    log(f"generated {len(lens)} requests ({T} tokens) in {time.time() - t0:.1f}s")
+    conv = lambda x: torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).cuda()
+    cat = lambda xs: conv(np.concatenate([x[0].reshape(-1) for x in xs]))
+    Qp, Kp, Vp = cat([s.Q for s in samples]), cat([s.K for s in samples]), cat([s.V for s in samples])
+    prob_r = M.make_problem(len(lens), Hq, Hkv, n_max, dh, "bf16", "f32")
+    O_r = torch.empty(Hq * T * dh, dtype=torch.float32, device="cuda")
+    kept_r = torch.zeros((len(lens), Hq), dtype=torch.int64, device="cuda")
+    status = torch.zeros(1, dtype=torch.int32, device="cuda")
+    ws_r = torch.empty(M.minf_ragged_ws_bytes(prob_r, heads), dtype=torch.uint8, device="cuda")
+    stream = torch.cuda.current_stream()
+
+    def timed(fn, steps):
+        fn()
+        ms = []
+        for _ in range(steps):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            fn()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            ms.append(e0.elapsed_time(e1))
+        return float(np.median(ms))
+
+    ms_r = timed(lambda: M.minf_prefill_ragged(prob_r, heads, lens, Qp, Kp, Vp, O_r, None, kept_r, status, ws_r),
+                 max(1, a.steps))
+    if int(status.item()) != 0:
+        raise RuntimeError(f"device status {int(status.item())}")
+    kept = int(kept_r.sum().item())
+    del Qp, Kp, Vp, O_r, ws_r
+    torch.cuda.empty_cache()
+    # the same prompts padded to the longest (zeros after each prompt)
+    Qd = torch.zeros((len(lens), Hq, n_max, dh), dtype=torch.int16, device="cuda")
+    Kd = torch.zeros((len(lens), Hkv, n_max, dh), dtype=torch.int16, device="cuda")
+    Vd = torch.zeros((len(lens), Hkv, n_max, dh), dtype=torch.int16, device="cuda")
+    for b, s in enumerate(samples):
+        n = s.n
+        Qd[b, :, :n] = conv(s.Q[0])
+        Kd[b, :, :n] = conv(s.K[0])
+        Vd[b, :, :n] = conv(s.V[0])
+    del samples
+    prob_p = M.make_problem(len(lens), Hq, Hkv, n_max, dh, "bf16", "f32")
+    buf = M.alloc_buffers(prob_p, heads)
+    O_p = torch.empty((len(lens), Hq, n_max, dh), dtype=torch.float32, device="cuda")
+    ms_p = timed(lambda: M.run_layer(prob_p, heads, Qd, Kd, Vd, O_p, buf=buf), max(1, a.steps))
+    out = {
+        "metric": "ragged batch prefill ms (8 prompts, 4K-64K tokens) vs the same batch padded to the longest",
+        "config": {"workload": "ragged8_planted_h32kv8_d128_bf16_mixed", "lens": lens, "tokens": T, "Hq": Hq,
+                   "Hkv": Hkv, "dh": dh, "heads": "the 128K layer's table: 16 vertical-slash, 8 block-sparse, "
+                                                  "8 A-shape"},
+        "data": "synthetic, seeded (planted sinks + periodic slashes), resident in HBM",
+        "ragged_ms": round(ms_r, 3),
+        "padded_ms": round(ms_p, 3),
+        "padded_over_ragged": round(ms_p / ms_r, 3),
+        "ragged_tokens_per_s": round(T / (ms_r * 1e-3), 1),
+        "ragged_kept_edges": kept,
+        "ragged_kept_edge_tflops": round(4 * dh * kept / (ms_r * 1e-3) / 1e12, 1),
+        "timing": "median of the timed runs after one warm-up run, warm caches; whole path (index, tiles, attention)",
+    }
+    print(json.dumps(out), flush=True)
+
+
 def crossover(a):
     """Sparse layer (index + attention, the 128K mixed pattern table) against
     the dense causal baseline over sequence lengths, on planted inputs of
@@ -315,7 +396,9 @@ def main():
     ap.add_argument("--no-exact", action="store_true", help="skip the exact slash pairs (slash_tile=1) layer")
     ap.add_argument("--search", type=int, default=0,
                     help="only run the offline pattern search on a calibration layer of this length")
-    ap.add_argument("--search-eps", type=float, default=0.05, help="output-error bound of the pattern search")
+    ap.add_argument("--search-eps", type=float, default=0.05, help="error bound of the pattern search")
+    ap.add_argument("--ragged", action="store_true",
+                    help="only time a ragged batch of 8 requests against the same batch padded to its longest")
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="only run a plain device copy of this many MiB (memory-counter calibration)")
     a = ap.parse_args()
@@ -332,6 +415,9 @@ def main():
         return
     if a.search:
         pattern_search(a)
+        return
+    if a.ragged:
+        ragged_batch(a)
         return
 
     import numpy as np

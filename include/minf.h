@@ -256,6 +256,32 @@ minf_status minf_output_error(const minf_problem* prob, const void* O, const voi
 minf_status minf_captured_mass(const minf_problem* prob, const float* lse, const float* lse_ref, double* mass,
                                void* stream);
 
+/* Ragged (variable-length) batch prefill: prob->B sequences of lengths
+ * seq_lens[b] (host array, each in [1, prob->n]), packed back to back with
+ * no padding (the serving case of the cost-model page, section 2.2: a batch
+ * padded to its longest request spends projection and attention work on the
+ * padding).  Sample b is the contiguous block at token offset
+ * t_b = sum_{c<b} seq_lens[c]:
+ *   Q, O: [Hq, len_b, dh] at element offset Hq*dh*t_b (input / output type),
+ *   K, V: [Hkv, len_b, dh] at element offset Hkv*dh*t_b,
+ *   lse:  [Hq, len_b] at offset Hq*t_b (fp32; NULL to skip),
+ * so the full tensors hold Hq*dh*sum(len) (resp. Hkv*dh*sum(len)) elements.
+ * Each sample runs the whole path (minf_vs_index, minf_bs_index,
+ * minf_build_tiles, minf_sparse_attn) as a problem of its own length with
+ * B = 1, on `stream`, one after another: indices are per sample and no
+ * window, slash or block crosses a sample boundary.
+ *   kept_edges: device [B, Hq] int64, E_h of each sample and head, or NULL;
+ *   status: device int32[1], zeroed by the call, then the OR of MINF_DEV_*
+ *     bits over all samples;
+ *   ws: device workspace of at least minf_ragged_ws_bytes(prob, heads)
+ *     bytes (index and tile buffers plus the stage workspace, all for one
+ *     sequence of length prob->n, reused by every sample).
+ * Errors as for the four calls; MINF_EINVAL for a length outside [1, n]. */
+minf_status minf_ragged_ws_bytes(const minf_problem* prob, const minf_head_cfg* heads, int64_t* ws_bytes);
+minf_status minf_prefill_ragged(const minf_problem* prob, const minf_head_cfg* heads, const int32_t* seq_lens,
+                                const void* Q, const void* K, const void* V, void* O, float* lse,
+                                int64_t* kept_edges, int32_t* status, void* ws, size_t ws_bytes, void* stream);
+
 /* Kernel timing, for measurement harnesses; computing never needs it.
  * After minf_timing_start(max_calls), each of the next max_calls calls of
  * minf_sparse_attn records a HIP event pair on its stream around its main

@@ -14,6 +14,8 @@ Entry points (same names and argument order as include/minf.h):
     minf_sparse_attn(prob, heads, Q, K, V, blk_idx, blk_cnt, tiles, O, lse, ws, stream=None)
     minf_output_error(prob, O, O_ref, err, stream=None)
     minf_captured_mass(prob, lse, lse_ref, mass, stream=None)
+    minf_ragged_ws_bytes(prob, heads) -> int
+    minf_prefill_ragged(prob, heads, seq_lens, Q, K, V, O, lse, kept_edges, status, ws, stream=None)
 The offline pattern search that drives them on calibration input is in
 long_context_prefill_amd.search.
 """
@@ -33,7 +35,8 @@ MINF_FORCE_FIRST_BLOCK, MINF_FORCE_DIAG_BLOCK = 1, 2
 MINF_DEV_BAD_VERTICAL, MINF_DEV_BAD_SLASH, MINF_DEV_BAD_BLOCK, MINF_DEV_CAPACITY = 1, 2, 4, 8
 
 EXPORTED = ["minf_query_sizes", "minf_vs_index", "minf_bs_index", "minf_build_tiles",
-            "minf_sparse_attn", "minf_output_error", "minf_captured_mass", "minf_timing_start",
+            "minf_sparse_attn", "minf_output_error", "minf_captured_mass", "minf_ragged_ws_bytes",
+            "minf_prefill_ragged", "minf_timing_start",
             "minf_timing_read", "minf_status_string", "minf_last_error", "minf_version"]
 
 
@@ -91,8 +94,11 @@ def load_library(path: str = LIB_PATH):
                                      vp, ctypes.c_size_t, vp]
     lib.minf_output_error.argtypes = [P(MinfProblem), vp, vp, vp, vp]
     lib.minf_captured_mass.argtypes = [P(MinfProblem), vp, vp, vp, vp]
+    lib.minf_ragged_ws_bytes.argtypes = [P(MinfProblem), P(MinfHeadCfg), P(ctypes.c_int64)]
+    lib.minf_prefill_ragged.argtypes = [P(MinfProblem), P(MinfHeadCfg), P(ctypes.c_int32), vp, vp, vp, vp, vp, vp, vp,
+                                        vp, ctypes.c_size_t, vp]
     for f in ("minf_query_sizes", "minf_vs_index", "minf_bs_index", "minf_build_tiles", "minf_sparse_attn",
-              "minf_output_error", "minf_captured_mass"):
+              "minf_output_error", "minf_captured_mass", "minf_ragged_ws_bytes", "minf_prefill_ragged"):
         getattr(lib, f).restype = ctypes.c_int
     lib.minf_timing_start.argtypes = [ctypes.c_int32]
     lib.minf_timing_start.restype = ctypes.c_int
@@ -207,6 +213,22 @@ def minf_captured_mass(prob, lse, lse_ref, mass, stream=None):
     exp(lse - lse_ref)."""
     lib = load_library()
     _check(lib.minf_captured_mass(ctypes.byref(prob), _ptr(lse), _ptr(lse_ref), _ptr(mass), _stream(stream)))
+
+
+def minf_ragged_ws_bytes(prob, heads) -> int:
+    lib = load_library()
+    out = ctypes.c_int64(0)
+    _check(lib.minf_ragged_ws_bytes(ctypes.byref(prob), heads, ctypes.byref(out)))
+    return int(out.value)
+
+
+def minf_prefill_ragged(prob, heads, seq_lens, Q, K, V, O, lse, kept_edges, status, ws, stream=None):
+    """seq_lens: a host sequence of prob.B lengths; tensors packed as
+    include/minf.h describes."""
+    lib = load_library()
+    lens = (ctypes.c_int32 * max(1, len(seq_lens)))(*[int(x) for x in seq_lens])
+    _check(lib.minf_prefill_ragged(ctypes.byref(prob), heads, lens, _ptr(Q), _ptr(K), _ptr(V), _ptr(O), _ptr(lse),
+                                   _ptr(kept_edges), _ptr(status), _ptr(ws), _nbytes(ws), _stream(stream)))
 
 
 def minf_timing_start(max_calls: int):

@@ -77,7 +77,18 @@ __global__ __launch_bounds__(256) void captured_mass_kernel(const float* lse, co
   if (threadIdx.x == 0) mass[blockIdx.x] = sm[0];
 }
 
+__global__ __launch_bounds__(256) void fill_i32_kernel(int32_t* p, int64_t n, int32_t v) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i < n) p[i] = v;
+}
+
 }  // namespace
+
+hipError_t launch_fill_i32(int32_t* p, int64_t n, int32_t v, hipStream_t st) {
+  if (n <= 0) return hipSuccess;
+  hipLaunchKernelGGL(fill_i32_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, p, n, v);
+  return hipGetLastError();
+}
 
 hipError_t launch_captured_mass(const float* lse, const float* lse_ref, int64_t heads, int64_t n, double* mass,
                                 hipStream_t st) {

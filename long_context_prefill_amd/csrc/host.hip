@@ -360,6 +360,42 @@ minf_status minf_sparse_attn(const minf_problem* prob, const minf_head_cfg* head
                     "minf_sparse_attn launch");
 }
 
+// ---- ragged batches: one workspace holds, for a single sequence of the
+// longest length, the index and tile buffers and the stage workspace; the
+// samples run one after another on the stream and reuse it.
+struct RaggedLayout {
+  size_t vert, slash, blk, blkcnt, span_lo, span_hi, span_cnt, chunk_lo, chunk_hi, chunk_cnt, cols, col_cnt,
+      sbits, cbits, kept, stage, total;
+};
+static minf_status ragged_layout(const minf_problem* prob, const minf_head_cfg* heads, RaggedLayout* L) {
+  minf_problem one = *prob;
+  one.B = 1;
+  Derived d;
+  minf_status s = validate(&one, heads, &d);
+  if (s != MINF_OK) return s;
+  const size_t Hq = (size_t)prob->Hq, nq = (size_t)d.nq;
+  size_t off = 0;
+  auto take = [&](size_t bytes) { const size_t o = off; off += (bytes + 255) & ~size_t(255); return o; };
+  L->vert = take(4 * Hq * std::max<int64_t>(d.max_v, 1));
+  L->slash = take(4 * Hq * std::max<int64_t>(d.max_s, 1));
+  L->blk = take(4 * Hq * nq * std::max<int64_t>(d.max_kb, 1));
+  L->blkcnt = take(4 * Hq * nq);
+  L->span_lo = take(4 * Hq * std::max<int64_t>(d.max_s, 1));
+  L->span_hi = take(4 * Hq * std::max<int64_t>(d.max_s, 1));
+  L->span_cnt = take(4 * Hq);
+  L->chunk_lo = take(4 * Hq * std::max<int64_t>(d.max_chunks, 1));
+  L->chunk_hi = take(4 * Hq * std::max<int64_t>(d.max_chunks, 1));
+  L->chunk_cnt = take(4 * Hq * nq);
+  L->cols = take(4 * Hq * nq * std::max<int64_t>(d.max_v, 1));
+  L->col_cnt = take(4 * Hq * nq);
+  L->sbits = take(4 * Hq * std::max<int64_t>(d.bits_words, 1));
+  L->cbits = take(4 * Hq * std::max<int64_t>(d.bits_words, 1));
+  L->kept = take(8 * Hq);
+  L->stage = take(ws_total(&one, d));
+  L->total = off;
+  return MINF_OK;
+}
+
 minf_status minf_output_error(const minf_problem* prob, const void* O, const void* O_ref, double* err, void* stream) {
   g_err[0] = 0;
   if (!prob || !O || !O_ref || !err) return fail(MINF_EINVAL, "null problem, O, O_ref or err");
@@ -384,6 +420,76 @@ minf_status minf_captured_mass(const minf_problem* prob, const float* lse, const
   return hip_status(minf::launch_captured_mass(lse, lse_ref, (int64_t)prob->B * prob->Hq, prob->n, mass,
                                                static_cast<hipStream_t>(stream)),
                     "minf_captured_mass launch");
+}
+
+minf_status minf_ragged_ws_bytes(const minf_problem* prob, const minf_head_cfg* heads, int64_t* ws_bytes) {
+  g_err[0] = 0;
+  if (!ws_bytes) return fail(MINF_EINVAL, "null ws_bytes");
+  RaggedLayout L;
+  const minf_status s = ragged_layout(prob, heads, &L);
+  if (s != MINF_OK) return s;
+  *ws_bytes = (int64_t)L.total;
+  return MINF_OK;
+}
+
+minf_status minf_prefill_ragged(const minf_problem* prob, const minf_head_cfg* heads, const int32_t* seq_lens,
+                                const void* Q, const void* K, const void* V, void* O, float* lse,
+                                int64_t* kept_edges, int32_t* status, void* ws, size_t ws_bytes, void* stream) {
+  g_err[0] = 0;
+  RaggedLayout L;
+  minf_status s = ragged_layout(prob, heads, &L);
+  if (s != MINF_OK) return s;
+  if (!seq_lens || !Q || !K || !V || !O || !status) return fail(MINF_EINVAL, "null seq_lens, Q, K, V, O or status");
+  for (int b = 0; b < prob->B; ++b)
+    if (seq_lens[b] < 1 || seq_lens[b] > prob->n)
+      return fail(MINF_EINVAL, "sequence %d has length %d, outside [1, n=%d]", b, seq_lens[b], prob->n);
+  if (!ws) return fail(MINF_EWORKSPACE, "workspace pointer is null");
+  if (ws_bytes < L.total) return fail(MINF_EWORKSPACE, "workspace of %zu bytes is smaller than the %zu needed", ws_bytes,
+                                      L.total);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  if ((s = hip_status(minf::launch_fill_i32(status, 1, 0, st), "status reset")) != MINF_OK) return s;
+  char* w = static_cast<char*>(ws);
+  const size_t in_sz = prob->in_dtype == MINF_BF16 ? 2 : 4, out_sz = prob->out_dtype == MINF_BF16 ? 2 : 4;
+  const size_t Hq = (size_t)prob->Hq, Hkv = (size_t)prob->Hkv, dh = (size_t)prob->dh;
+  size_t off = 0;   // tokens before sample b
+  for (int b = 0; b < prob->B; ++b) {
+    minf_problem one = *prob;
+    one.B = 1;
+    one.n = seq_lens[b];
+    minf_tiles t{};
+    t.span_lo = reinterpret_cast<int32_t*>(w + L.span_lo);
+    t.span_hi = reinterpret_cast<int32_t*>(w + L.span_hi);
+    t.span_cnt = reinterpret_cast<int32_t*>(w + L.span_cnt);
+    t.chunk_lo = reinterpret_cast<int32_t*>(w + L.chunk_lo);
+    t.chunk_hi = reinterpret_cast<int32_t*>(w + L.chunk_hi);
+    t.chunk_cnt = reinterpret_cast<int32_t*>(w + L.chunk_cnt);
+    t.cols = reinterpret_cast<int32_t*>(w + L.cols);
+    t.col_cnt = reinterpret_cast<int32_t*>(w + L.col_cnt);
+    t.slash_bits = reinterpret_cast<uint32_t*>(w + L.sbits);
+    t.col_bits = reinterpret_cast<uint32_t*>(w + L.cbits);
+    t.status = status;
+    // kept edges of this sample go straight to the caller's [B, Hq] array,
+    // or to a scratch row of the workspace
+    t.kept_edges = kept_edges ? kept_edges + (size_t)b * Hq : reinterpret_cast<int64_t*>(w + L.kept);
+    int32_t* vert = reinterpret_cast<int32_t*>(w + L.vert);
+    int32_t* slash = reinterpret_cast<int32_t*>(w + L.slash);
+    int32_t* blk = reinterpret_cast<int32_t*>(w + L.blk);
+    int32_t* blkcnt = reinterpret_cast<int32_t*>(w + L.blkcnt);
+    void* stage = w + L.stage;
+    const size_t stage_bytes = L.total - L.stage;
+    const char* Qb = static_cast<const char*>(Q) + in_sz * Hq * dh * off;
+    const char* Kb = static_cast<const char*>(K) + in_sz * Hkv * dh * off;
+    const char* Vb = static_cast<const char*>(V) + in_sz * Hkv * dh * off;
+    char* Ob = static_cast<char*>(O) + out_sz * Hq * dh * off;
+    float* lb = lse ? lse + Hq * off : nullptr;
+    if ((s = minf_vs_index(&one, heads, Qb, Kb, vert, slash, nullptr, nullptr, stage, stage_bytes, stream)) != MINF_OK ||
+        (s = minf_bs_index(&one, heads, Qb, Kb, blk, blkcnt, stage, stage_bytes, stream)) != MINF_OK ||
+        (s = minf_build_tiles(&one, heads, vert, slash, blk, blkcnt, &t, stage, stage_bytes, stream)) != MINF_OK ||
+        (s = minf_sparse_attn(&one, heads, Qb, Kb, Vb, blk, blkcnt, &t, Ob, lb, stage, stage_bytes, stream)) != MINF_OK)
+      return s;
+    off += (size_t)seq_lens[b];
+  }
+  return MINF_OK;
 }
 
 minf_status minf_timing_start(int32_t max_calls) {

@@ -147,6 +147,9 @@ hipError_t launch_bs_index(const BsParams& p, hipStream_t st);
 // `heads` blocks of `per_head` elements (error.hip).
 hipError_t launch_output_error(const void* O, const void* R, int64_t heads, int64_t per_head, bool bf16, double* err,
                                hipStream_t st);
+// p[0 .. n) = v, a plain kernel (no memset node when a caller captures a
+// graph) (error.hip).
+hipError_t launch_fill_i32(int32_t* p, int64_t n, int32_t v, hipStream_t st);
 // Per-head fp64 sum over n rows of exp(lse - lse_ref) (error.hip).
 hipError_t launch_captured_mass(const float* lse, const float* lse_ref, int64_t heads, int64_t n, double* mass,
                                 hipStream_t st);

@@ -161,3 +161,31 @@ def test_output_error_rejects_bad_arguments(lib):
     p0 = _prob(n=0)
     assert lib.minf_output_error(ctypes.byref(p0), fake, fake, fake, None) == M.MINF_EINVAL
     assert lib.minf_last_error().decode()
+
+
+def test_ragged_rejects_bad_arguments(lib):
+    """minf_prefill_ragged validates lengths, pointers and the workspace
+    before any launch (the fake pointers are never dereferenced)."""
+    fake = 0x1000
+    p = _prob(B=3)
+    h = M.make_heads(HEADS)
+    need = M.minf_ragged_ws_bytes(p, h)
+    one = M.minf_query_sizes(_prob(B=1), h)
+    assert need >= one.ws_bytes
+    def call(lens, Q=fake, O=fake, status=fake, ws=fake, ws_bytes=need):
+        arr = None if lens is None else (ctypes.c_int32 * len(lens))(*lens)
+        return lib.minf_prefill_ragged(ctypes.byref(p), h, arr, Q, fake, fake, O, None, None, status, ws, ws_bytes,
+                                       None)
+    assert call(None) == M.MINF_EINVAL
+    assert call([10, 0, 7]) == M.MINF_EINVAL              # an empty sequence
+    assert call([10, 1001, 7]) == M.MINF_EINVAL           # longer than n
+    assert "length" in lib.minf_last_error().decode()
+    assert call([10, 1000, 7], Q=None) == M.MINF_EINVAL
+    assert call([10, 1000, 7], O=None) == M.MINF_EINVAL
+    assert call([10, 1000, 7], status=None) == M.MINF_EINVAL
+    assert call([10, 1000, 7], ws=None) == M.MINF_EWORKSPACE
+    assert call([10, 1000, 7], ws_bytes=need - 1) == M.MINF_EWORKSPACE
+    # a bad head table is refused like everywhere else
+    bad = M.make_heads([gen.HeadCfg(7)] + HEADS[1:])
+    assert lib.minf_prefill_ragged(ctypes.byref(p), bad, (ctypes.c_int32 * 3)(1, 2, 3), fake, fake, fake, fake,
+                                   None, None, fake, fake, need, None) == M.MINF_EINVAL
