@@ -213,7 +213,7 @@ def time_layer(M, prob, heads, Q, K, V, O_, steps, warmup, index=True, flush=Non
     return float(np.median(ms)), kept
 
 
-def pattern_search(a):
+def pattern_search(a, n):
     """The offline kernel-aware pattern search on a synthetic calibration layer
     (KV groups with local, planted and clustered structure), B=1, Hq=32,
     Hkv=8, dh=128, bf16, length a.search; one JSON line."""
@@ -222,7 +222,6 @@ def pattern_search(a):
     import long_context_prefill_amd as M
     from long_context_prefill_amd import search as S
     from synth import gen
-    n = a.search
     t0 = time.time()
     p = gen.make_calibration(n=n, Hq=32, Hkv=8, dh=128, dtype="bf16")
     log(f"generated {p.name} in {time.time() - t0:.1f}s")
@@ -261,7 +260,7 @@ def pattern_search(a):
             for g in sorted(set(p.meta["group_kinds"]))},
         "timing": "median of the timed runs after one warm-up run, warm caches; each candidate on all heads",
     }
-    print(json.dumps(out), flush=True)
+    return out
 
 
 RAGGED_LENS = [65536, 8192, 32768, 4096, 16384, 49152, 12288, 24576]
@@ -342,7 +341,7 @@ def ragged_batch(a):
         "ragged_kept_edge_tflops": round(4 * dh * kept / (ms_r * 1e-3) / 1e12, 1),
         "timing": "median of the timed runs after one warm-up run, warm caches; whole path (index, tiles, attention)",
     }
-    print(json.dumps(out), flush=True)
+    return out
 
 
 def crossover(a):
@@ -394,6 +393,8 @@ def main():
                     help="comma-separated lengths: time the sparse layer against the dense causal baseline")
     ap.add_argument("--no-dense", action="store_true", help="skip the dense causal baseline")
     ap.add_argument("--no-exact", action="store_true", help="skip the exact slash pairs (slash_tile=1) layer")
+    ap.add_argument("--no-search", action="store_true", help="skip the pattern search summary (32K calibration layer)")
+    ap.add_argument("--no-ragged", action="store_true", help="skip the ragged batch summary")
     ap.add_argument("--search", type=int, default=0,
                     help="only run the offline pattern search on a calibration layer of this length")
     ap.add_argument("--search-eps", type=float, default=0.05, help="error bound of the pattern search")
@@ -414,10 +415,10 @@ def main():
         crossover(a)
         return
     if a.search:
-        pattern_search(a)
+        print(json.dumps(pattern_search(a, a.search)), flush=True)
         return
     if a.ragged:
-        ragged_batch(a)
+        print(json.dumps(ragged_batch(a)), flush=True)
         return
 
     import numpy as np
@@ -532,6 +533,23 @@ def main():
                          "steps"}
         log(f"exact slash pairs in {time.time() - t0:.1f}s")
 
+    search = None
+    if not a.no_search:
+        t0 = time.time()
+        r = pattern_search(argparse.Namespace(steps=3, search_eps=a.search_eps), 32768)
+        search = {k: r[k] for k in ("config", "eps", "measure", "dense_ms", "table_ms", "speedup_vs_dense",
+                                    "table_kinds", "max_table_missed_mass", "max_table_rel_err")}
+        search["what"] = ("offline kernel-aware pattern search on a 32K calibration layer (local, planted and "
+                          "clustered KV groups); bench.py --search 32768 prints every candidate")
+        log(f"pattern search in {time.time() - t0:.1f}s")
+    ragged = None
+    if not a.no_ragged:
+        t0 = time.time()
+        r = ragged_batch(argparse.Namespace(steps=3))
+        ragged = {k: r[k] for k in ("config", "ragged_ms", "padded_ms", "padded_over_ragged", "ragged_tokens_per_s",
+                                    "ragged_kept_edge_tflops")}
+        log(f"ragged batch in {time.time() - t0:.1f}s")
+
     cpu = None
     if not a.no_cpu_baseline:
         try:
@@ -584,6 +602,8 @@ def main():
                      "launches_timed": len(kern)},
         "dense_baseline": dense_bl,
         "exact_slash_pairs": exact,
+        "pattern_search": search,
+        "ragged_batch": ragged,
         "cpu_baseline": cpu,
         "context": "pages: up to 10x prefill speedup over dense on an A100 (another machine and workload)",
     }
