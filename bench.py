@@ -533,6 +533,25 @@ def main():
                          "steps"}
         log(f"exact slash pairs in {time.time() - t0:.1f}s")
 
+    vs_fused = None
+    if "vslash" in per_kind:
+        # the Vertical-Slash estimate alone, warm: the two-launch path the layer
+        # uses against the single-launch proxy (minf_vs_index_fused)
+        def vs_ms(fn, reps=20):
+            fn(prob, heads, Q, K, buf["vert_idx"], buf["slash_idx"], None, None, buf["ws"], stream=stream)
+            ms = []
+            for _ in range(reps):
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record(stream)
+                fn(prob, heads, Q, K, buf["vert_idx"], buf["slash_idx"], None, None, buf["ws"], stream=stream)
+                e1.record(stream)
+                e1.synchronize()
+                ms.append(e0.elapsed_time(e1))
+            return sorted(ms)[reps // 2]
+        two, one = vs_ms(M.minf_vs_index), vs_ms(M.minf_vs_index_fused)
+        vs_fused = {"two_launch_ms": round(two, 4), "single_launch_ms": round(one, 4),
+                    "what": "Vertical-Slash estimate (proxy, fold, column and slash sums, top-k) alone, warm, "
+                            "median of 20: minf_vs_index (the layer's path) vs minf_vs_index_fused"}
     search = None
     if not a.no_search:
         t0 = time.time()
@@ -602,6 +621,7 @@ def main():
                      "launches_timed": len(kern)},
         "dense_baseline": dense_bl,
         "exact_slash_pairs": exact,
+        "vs_single_launch": vs_fused,
         "pattern_search": search,
         "ragged_batch": ragged,
         "cpu_baseline": cpu,

@@ -186,6 +186,22 @@ minf_status minf_vs_index(const minf_problem* prob, const minf_head_cfg* heads,
                           float* vert_score, float* slash_score,
                           void* ws, size_t ws_bytes, void* stream);
 
+/* The same Vertical-Slash estimation with the proxy in one launch (the
+ * conclusion of the cost-model page on the index stage: fewer read and write
+ * rounds and synchronisations between the reduce and the selection): the
+ * per-row LSE fold and the column and slash sums run in the same grid as the
+ * proxy scores, a work-group of the second pass waiting (bounded) for its
+ * head's LSE.  Arguments, outputs, workspace and errors as minf_vs_index;
+ * scores equal minf_vs_index's up to the summation order of the LSE and slash
+ * sums, so selections can differ only between near-equal scores.  The
+ * two-launch minf_vs_index is faster on MI355X and remains the path that
+ * minf_prefill_ragged and the layer use. */
+minf_status minf_vs_index_fused(const minf_problem* prob, const minf_head_cfg* heads,
+                                const void* Q, const void* K,
+                                int32_t* vert_idx, int32_t* slash_idx,
+                                float* vert_score, float* slash_score,
+                                void* ws, size_t ws_bytes, void* stream);
+
 /* Block-Sparse index estimation (MInference page, section 2, Eq. 6 and the
  * mean-pooling proxy; blog section 2.3.2).  For every BS head: Q and K are
  * mean-pooled over 64-row blocks (the last block over its true length),

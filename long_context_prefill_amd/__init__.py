@@ -9,6 +9,7 @@ raises - there is no fallback implementation.
 Entry points (same names and argument order as include/minf.h):
     minf_query_sizes(prob, heads) -> MinfSizes
     minf_vs_index(prob, heads, Q, K, vert_idx, slash_idx, vert_score, slash_score, ws, stream=None)
+    minf_vs_index_fused(...)   same, the proxy in one launch
     minf_bs_index(prob, heads, Q, K, blk_idx, blk_cnt, ws, stream=None)
     minf_build_tiles(prob, heads, vert_idx, slash_idx, blk_idx, blk_cnt, tiles, ws, stream=None)
     minf_sparse_attn(prob, heads, Q, K, V, blk_idx, blk_cnt, tiles, O, lse, ws, stream=None)
@@ -34,7 +35,7 @@ MINF_ASHAPE, MINF_VSLASH, MINF_BSPARSE = 0, 1, 2
 MINF_FORCE_FIRST_BLOCK, MINF_FORCE_DIAG_BLOCK = 1, 2
 MINF_DEV_BAD_VERTICAL, MINF_DEV_BAD_SLASH, MINF_DEV_BAD_BLOCK, MINF_DEV_CAPACITY = 1, 2, 4, 8
 
-EXPORTED = ["minf_query_sizes", "minf_vs_index", "minf_bs_index", "minf_build_tiles",
+EXPORTED = ["minf_query_sizes", "minf_vs_index", "minf_vs_index_fused", "minf_bs_index", "minf_build_tiles",
             "minf_sparse_attn", "minf_output_error", "minf_captured_mass", "minf_ragged_ws_bytes",
             "minf_prefill_ragged", "minf_timing_start",
             "minf_timing_read", "minf_status_string", "minf_last_error", "minf_version"]
@@ -87,6 +88,7 @@ def load_library(path: str = LIB_PATH):
     vp = ctypes.c_void_p
     lib.minf_query_sizes.argtypes = [P(MinfProblem), P(MinfHeadCfg), P(MinfSizes)]
     lib.minf_vs_index.argtypes = [P(MinfProblem), P(MinfHeadCfg), vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t, vp]
+    lib.minf_vs_index_fused.argtypes = lib.minf_vs_index.argtypes
     lib.minf_bs_index.argtypes = [P(MinfProblem), P(MinfHeadCfg), vp, vp, vp, vp, vp, ctypes.c_size_t, vp]
     lib.minf_build_tiles.argtypes = [P(MinfProblem), P(MinfHeadCfg), vp, vp, vp, vp, P(MinfTiles), vp,
                                      ctypes.c_size_t, vp]
@@ -97,7 +99,8 @@ def load_library(path: str = LIB_PATH):
     lib.minf_ragged_ws_bytes.argtypes = [P(MinfProblem), P(MinfHeadCfg), P(ctypes.c_int64)]
     lib.minf_prefill_ragged.argtypes = [P(MinfProblem), P(MinfHeadCfg), P(ctypes.c_int32), vp, vp, vp, vp, vp, vp, vp,
                                         vp, ctypes.c_size_t, vp]
-    for f in ("minf_query_sizes", "minf_vs_index", "minf_bs_index", "minf_build_tiles", "minf_sparse_attn",
+    for f in ("minf_query_sizes", "minf_vs_index", "minf_vs_index_fused", "minf_bs_index", "minf_build_tiles",
+              "minf_sparse_attn",
               "minf_output_error", "minf_captured_mass", "minf_ragged_ws_bytes", "minf_prefill_ragged"):
         getattr(lib, f).restype = ctypes.c_int
     lib.minf_timing_start.argtypes = [ctypes.c_int32]
@@ -177,6 +180,13 @@ def minf_vs_index(prob, heads, Q, K, vert_idx, slash_idx, vert_score=None, slash
     lib = load_library()
     _check(lib.minf_vs_index(ctypes.byref(prob), heads, _ptr(Q), _ptr(K), _ptr(vert_idx), _ptr(slash_idx),
                              _ptr(vert_score), _ptr(slash_score), _ptr(ws), _nbytes(ws), _stream(stream)))
+
+
+def minf_vs_index_fused(prob, heads, Q, K, vert_idx, slash_idx, vert_score=None, slash_score=None, ws=None,
+                        stream=None):
+    lib = load_library()
+    _check(lib.minf_vs_index_fused(ctypes.byref(prob), heads, _ptr(Q), _ptr(K), _ptr(vert_idx), _ptr(slash_idx),
+                                   _ptr(vert_score), _ptr(slash_score), _ptr(ws), _nbytes(ws), _stream(stream)))
 
 
 def minf_bs_index(prob, heads, Q, K, blk_idx, blk_cnt, ws=None, stream=None):

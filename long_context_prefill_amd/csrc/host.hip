@@ -236,9 +236,9 @@ minf_status minf_query_sizes(const minf_problem* prob, const minf_head_cfg* head
   return MINF_OK;
 }
 
-minf_status minf_vs_index(const minf_problem* prob, const minf_head_cfg* heads, const void* Q, const void* K,
-                          int32_t* vert_idx, int32_t* slash_idx, float* vert_score, float* slash_score,
-                          void* ws, size_t ws_bytes, void* stream) {
+static minf_status vs_index_impl(const minf_problem* prob, const minf_head_cfg* heads, const void* Q, const void* K,
+                                 int32_t* vert_idx, int32_t* slash_idx, float* vert_score, float* slash_score,
+                                 void* ws, size_t ws_bytes, void* stream, bool fused) {
   Derived d;
   minf_status s = validate(prob, heads, &d);
   if (s != MINF_OK) return s;
@@ -256,7 +256,21 @@ minf_status minf_vs_index(const minf_problem* prob, const minf_head_cfg* heads, 
   v.ht = d.ht;
   v.ws = vs_ws(prob, d);
   v.ws_base = static_cast<char*>(ws);
-  return hip_status(minf::launch_vs_index(v, static_cast<hipStream_t>(stream)), "minf_vs_index launch");
+  const hipStream_t st = static_cast<hipStream_t>(stream);
+  return fused ? hip_status(minf::launch_vs_index_fused(v, st), "minf_vs_index_fused launch")
+               : hip_status(minf::launch_vs_index(v, st), "minf_vs_index launch");
+}
+
+minf_status minf_vs_index(const minf_problem* prob, const minf_head_cfg* heads, const void* Q, const void* K,
+                          int32_t* vert_idx, int32_t* slash_idx, float* vert_score, float* slash_score,
+                          void* ws, size_t ws_bytes, void* stream) {
+  return vs_index_impl(prob, heads, Q, K, vert_idx, slash_idx, vert_score, slash_score, ws, ws_bytes, stream, false);
+}
+
+minf_status minf_vs_index_fused(const minf_problem* prob, const minf_head_cfg* heads, const void* Q, const void* K,
+                                int32_t* vert_idx, int32_t* slash_idx, float* vert_score, float* slash_score,
+                                void* ws, size_t ws_bytes, void* stream) {
+  return vs_index_impl(prob, heads, Q, K, vert_idx, slash_idx, vert_score, slash_score, ws, ws_bytes, stream, true);
 }
 
 minf_status minf_bs_index(const minf_problem* prob, const minf_head_cfg* heads, const void* Q, const void* K,

@@ -103,6 +103,7 @@ constexpr int kVsDiagSlots = kVsWaveKeys + 64;    // diagonal partials per wave
 constexpr int kTopkSeg = 8192;                    // array elements per top-k work-group
 struct VsWs {
   size_t part_m, part_l, lse2, cbuf, rbuf, dpart;
+  size_t sync;                                    // work ticket and per-head counters of the single-launch proxy
   size_t tk_state, tk_hist, tk_cnt;               // multi-work-group top-k of c and r
   size_t total;
   int64_t nslots;                                 // proxy waves per head
@@ -125,6 +126,7 @@ struct VsParams {
   char* ws_base;
 };
 hipError_t launch_vs_index(const VsParams& p, hipStream_t st);
+hipError_t launch_vs_index_fused(const VsParams& p, hipStream_t st);   // the proxy in one launch
 
 // ---------------------------------------------------------------- BS index
 struct BsParams {

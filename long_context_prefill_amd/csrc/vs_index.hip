@@ -19,7 +19,10 @@
 //          wave through a small LDS tile, then written as partials;
 //  diag    each offset's two neighbouring partials are added in a fixed order;
 //  top-k   exact radix select per (head, score array).
+// minf_vs_index_fused runs pass 1, the fold and pass 2 in one launch instead
+// (described with its kernel below); the selection is shared.
 // No floating-point atomics are used, so two runs give identical bits.
+#include <algorithm>
 #include <type_traits>
 
 #include "kernels.h"
@@ -40,6 +43,7 @@ VsWs vs_workspace(int B, int Hq, int n, int nq) {
   w.cbuf = take(BH * (size_t)n * 4);
   w.rbuf = take(BH * (size_t)n * 4);
   w.dpart = take(BH * w.nslots * kVsDiagSlots * 4);
+  w.sync = take((1 + 2 * BH) * 4);
   w.tk_segs = ((int64_t)n + kTopkSeg - 1) / kTopkSeg;
   w.tk_state = take(2 * BH * 4 * 4);
   w.tk_hist = take(2 * BH * w.tk_segs * 256 * 4);
@@ -311,6 +315,351 @@ __global__ __launch_bounds__(256) void vs_diag_kernel(VsParams P) {
   rdst[(size_t)bh * n + d] = acc;
 }
 
+// Values exchanged between work-groups of the fused proxy (partials, LSE,
+// counters, flags) are read and written with agent-scope atomic loads and
+// stores: they bypass the per-XCD L2, which is not coherent across XCDs, so
+// no cache-wide write-back or invalidate is needed; a store is complete
+// (visible to the whole GPU) once the issuing wave's memory counter drains.
+__device__ __forceinline__ void put_c(float* p, float v) {
+  __hip_atomic_store(reinterpret_cast<int*>(p), __float_as_int(v), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float get_c(const float* p) {
+  return __int_as_float(
+      __hip_atomic_load(reinterpret_cast<const int*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+}
+// wait until this wave's memory operations have completed
+__device__ __forceinline__ void drain() { __builtin_amdgcn_s_waitcnt(0); }
+
+// ---------------------------------------------------------------- single-launch proxy
+// The same proxy in one launch (minf_vs_index_fused): pass 1, the LSE fold
+// and pass 2 run in one grid, a pass 2 work-group waiting for its head's
+// LSE.  Same results up to the summation order of the LSE and slash sums.
+// One task: the kVsGroupKeys consecutive keys of key range `range` of VS head
+// bh, four waves of kVsWaveKeys keys each.
+// PASS 1: running (max, sum) of the sampled rows per wave, combined into one
+// partial per work-group.
+// PASS 2: exact probabilities; each wave writes the column sums of its keys
+// and the complete slash sums of its kVsWaveKeys home offsets, the offsets d whose
+// largest key n - 1 - d lies in the wave's keys (their other keys lie at most
+// 63 below, which the wave also scores), so every offset is summed by one
+// wave in a fixed order.
+template <typename T, int DH, int PASS>
+__device__ __forceinline__ void fused_task(const VsParams& P, int bh, int range, float (*ptile)[33],
+                                           float (*red)[4][64], float* dacc) {
+  using Ops = ProxyOps<T, DH>;
+  const int gsz = P.Hq / P.Hkv;
+  const int h = bh % P.Hq;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int r16 = lane & 15, g = lane >> 4;
+  const int n = P.n;
+  const int L = min(P.ht.a[h], n);
+  const int b = bh / P.Hq;
+  const int kv = h / gsz;
+  const T* Qb = reinterpret_cast<const T*>(P.Q) + (size_t)bh * n * DH;
+  const T* Kb = reinterpret_cast<const T*>(P.K) + ((size_t)b * P.Hkv + kv) * n * DH;
+  const int J0 = (range * 4 + wave) * kVsWaveKeys;
+  if (PASS == 2 && J0 >= n) return;
+  const int J1 = min(J0 + kVsWaveKeys, n);
+  const int row_base = n - L;    // sampled row r is query n - L + r (valid for r < L)
+
+  typename Ops::QOp q[4][Ops::KS];
+  #pragma unroll
+  for (int nb = 0; nb < 4; ++nb) {
+    const int r = 16 * nb + r16;
+    if (r < L) Ops::load_k(Qb, row_base + r, g, q[nb]);
+    else Ops::zero(q[nb]);
+  }
+
+  float m_run[4], l_run[4], lse2[4];
+  #pragma unroll
+  for (int nb = 0; nb < 4; ++nb) { m_run[nb] = kNegInf; l_run[nb] = 0.f; lse2[nb] = 0.f; }
+  float* cdst = P.vert_score ? P.vert_score : reinterpret_cast<float*>(P.ws_base + P.ws.cbuf);
+  cdst += (size_t)bh * n;
+  if constexpr (PASS == 2) {
+    #pragma unroll
+    for (int qd = 0; qd < kVsWaveKeys / 64; ++qd) dacc[lane + 64 * qd] = 0.f;
+  }
+  if constexpr (PASS == 2) {
+    const float* l2 = reinterpret_cast<const float*>(P.ws_base + P.ws.lse2) + (size_t)bh * 64;
+    #pragma unroll
+    for (int nb = 0; nb < 4; ++nb) lse2[nb] = get_c(l2 + 16 * nb + r16);
+  }
+
+  // pass 2 also scores the 64 keys below the range: they complete the slash
+  // sums of the wave's home offsets (columns are written for j >= J0 only)
+  // the keys of the next step are loaded while this step is computed
+  const int jbeg = PASS == 2 ? max(0, J0 - 64) : J0;
+  typename Ops::QOp kop[2][Ops::KS];
+  #pragma unroll
+  for (int hh = 0; hh < 2; ++hh) Ops::load_k(Kb, min(jbeg + 16 * hh + r16, n - 1), g, kop[hh]);
+  for (int j = jbeg; j < J1; j += 32) {
+    typename Ops::QOp knext[2][Ops::KS];
+    #pragma unroll
+    for (int hh = 0; hh < 2; ++hh) Ops::load_k(Kb, min(j + 32 + 16 * hh + r16, n - 1), g, knext[hh]);
+    floatx4 s[2][4];
+    #pragma unroll
+    for (int hh = 0; hh < 2; ++hh)
+      #pragma unroll
+      for (int nb = 0; nb < 4; ++nb) s[hh][nb] = Ops::dot(kop[hh], q[nb]);
+    // valid pairs: sampled row r < L, key < n, key <= query index
+    const bool need_mask = (L < 64) || (j + 31 > row_base);
+    if (need_mask) {
+      #pragma unroll
+      for (int nb = 0; nb < 4; ++nb) {
+        const int r = 16 * nb + r16;
+        #pragma unroll
+        for (int hh = 0; hh < 2; ++hh)
+          #pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int key = j + 16 * hh + 4 * g + i;
+            if (!(r < L && key < n && key <= row_base + r)) s[hh][nb][i] = kNegInf;
+          }
+      }
+    }
+    if constexpr (PASS == 1) {
+      #pragma unroll
+      for (int nb = 0; nb < 4; ++nb) {
+        float x = fmaxf(fmaxf(fmaxf(s[0][nb][0], s[0][nb][1]), fmaxf(s[0][nb][2], s[0][nb][3])),
+                        fmaxf(fmaxf(s[1][nb][0], s[1][nb][1]), fmaxf(s[1][nb][2], s[1][nb][3])));
+        x = fmaxf(x, __shfl_xor(x, 16));
+        x = fmaxf(x, __shfl_xor(x, 32));
+        x *= P.c;
+        if (x > m_run[nb]) {
+          l_run[nb] *= fast_exp2(m_run[nb] - x);   // m_run = -inf gives 0
+          m_run[nb] = x;
+        }
+        const float msub = (m_run[nb] == kNegInf) ? 0.f : m_run[nb];
+        float ls = 0.f;
+        #pragma unroll
+        for (int hh = 0; hh < 2; ++hh)
+          #pragma unroll
+          for (int i = 0; i < 4; ++i) ls += fast_exp2(__builtin_fmaf(s[hh][nb][i], P.c, -msub));
+        l_run[nb] += ls;
+      }
+    } else {
+      // probabilities in place of the scores
+      #pragma unroll
+      for (int nb = 0; nb < 4; ++nb)
+        #pragma unroll
+        for (int hh = 0; hh < 2; ++hh)
+          #pragma unroll
+          for (int i = 0; i < 4; ++i) s[hh][nb][i] = fast_exp2(__builtin_fmaf(s[hh][nb][i], P.c, -lse2[nb]));
+      // column sums: over the 4 row groups in the lane, then over the 16 lanes of the row group
+      float cs[2][4];
+      #pragma unroll
+      for (int hh = 0; hh < 2; ++hh)
+        #pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          float x = (s[hh][0][i] + s[hh][1][i]) + (s[hh][2][i] + s[hh][3][i]);
+          x += __shfl_xor(x, 1);
+          x += __shfl_xor(x, 2);
+          x += __shfl_xor(x, 4);
+          x += __shfl_xor(x, 8);
+          cs[hh][i] = x;
+        }
+      // lane r16 < 8 writes key 16*(r16/4) + 4g + r16%4
+      if (r16 < 8 && j >= J0) {
+        const int hh = r16 >> 2, i = r16 & 3;
+        float val = 0.f;
+        #pragma unroll
+        for (int a = 0; a < 2; ++a)
+          #pragma unroll
+          for (int bq = 0; bq < 4; ++bq)
+            if (a == hh && bq == i) val = cs[a][bq];
+        const int key = j + 16 * hh + 4 * g + i;
+        if (key < n) cdst[key] = val;
+      }
+      // diagonal partials: tile[r][jl] = p(row r, key j + jl)
+      #pragma unroll
+      for (int nb = 0; nb < 4; ++nb)
+        #pragma unroll
+        for (int hh = 0; hh < 2; ++hh)
+          #pragma unroll
+          for (int i = 0; i < 4; ++i) ptile[16 * nb + r16][16 * hh + 4 * g + i] = s[hh][nb][i];
+      // the tile is private to this wave: LDS accesses of one wave complete in
+      // issue order, so a wave-scope fence (no work-group barrier: waves of a
+      // group may run different trip counts) orders the writes before the reads
+      __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      // the tile's 95 diagonals c = r - jl in [-31, 63], 32 elements per lane:
+      // lane l sums c1 = l - 31 and, for l < 31, c2 = l + 33, rows ascending
+      float s1 = 0.f, s2 = 0.f;
+      #pragma unroll 8
+      for (int k = 0; k < 32; ++k) {
+        const bool first = lane >= 31 || k <= lane;
+        const int r = lane >= 31 ? lane - 31 + k : (k <= lane ? k : k + 32);
+        const int jl = lane >= 31 ? k : (k <= lane ? k + 31 - lane : k - lane - 1);
+        const float v = ptile[r][jl];
+        if (first) s1 += v; else s2 += v;
+      }
+      // home slot t (offset d = n - kVsWaveKeys - J0 + t) lies on c = base + t here
+      const int base = L - kVsWaveKeys + (j - J0);
+      const int t1 = lane - 31 - base, t2 = lane + 33 - base;
+      if (t1 >= 0 && t1 < kVsWaveKeys) dacc[t1] += s1;
+      if (lane < 31 && t2 >= 0 && t2 < kVsWaveKeys) dacc[t2] += s2;
+      __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+    }
+    #pragma unroll
+    for (int hh = 0; hh < 2; ++hh)
+      #pragma unroll
+      for (int k = 0; k < Ops::KS; ++k) kop[hh][k] = knext[hh][k];
+  }
+
+  if constexpr (PASS == 1) {
+    #pragma unroll
+    for (int nb = 0; nb < 4; ++nb) {
+      l_run[nb] += __shfl_xor(l_run[nb], 16);
+      l_run[nb] += __shfl_xor(l_run[nb], 32);
+    }
+    // the four waves' partials are combined in wave order: one (max, sum)
+    // per row and work-group
+    if (g == 0) {
+      #pragma unroll
+      for (int nb = 0; nb < 4; ++nb) {
+        red[0][wave][16 * nb + r16] = m_run[nb];
+        red[1][wave][16 * nb + r16] = l_run[nb];
+      }
+    }
+    __syncthreads();
+    if (threadIdx.x < 64) {
+      const int r = threadIdx.x;
+      float M = red[0][0][r];
+      #pragma unroll
+      for (int w = 1; w < 4; ++w) M = fmaxf(M, red[0][w][r]);
+      float S = 0.f;
+      if (M != kNegInf) {
+        #pragma unroll
+        for (int w = 0; w < 4; ++w) S += red[1][w][r] * fast_exp2(red[0][w][r] - M);
+      }
+      float* pm = reinterpret_cast<float*>(P.ws_base + P.ws.part_m) + (size_t)bh * 64 * P.ws.nslots;
+      float* pl = reinterpret_cast<float*>(P.ws_base + P.ws.part_l) + (size_t)bh * 64 * P.ws.nslots;
+      put_c(pm + (size_t)r * P.ws.nslots + range, M);
+      put_c(pl + (size_t)r * P.ws.nslots + range, S);
+    }
+  } else {
+    float* rdst = P.slash_score ? P.slash_score : reinterpret_cast<float*>(P.ws_base + P.ws.rbuf);
+    rdst += (size_t)bh * n;
+    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    #pragma unroll
+    for (int qd = 0; qd < kVsWaveKeys / 64; ++qd) {
+      const int d = n - kVsWaveKeys - J0 + lane + 64 * qd;
+      if (d >= 0) rdst[d] = dacc[lane + 64 * qd];
+    }
+  }
+}
+
+// LSE of the 64 sampled rows of head bh from its per-work-group partials:
+// thread (row r, quarter q) takes slots q, q+4, ...; the row maximum first
+// (exact in any order), then the rescaled sums in slot order, the quarters
+// added by a fixed butterfly (each step commutative, so the four lanes agree).
+__device__ __forceinline__ void fused_fold(const VsParams& P, int bh, int nslots_used) {
+  const int r = threadIdx.x >> 2, q = threadIdx.x & 3;
+  const float* pm = reinterpret_cast<const float*>(P.ws_base + P.ws.part_m) + ((size_t)bh * 64 + r) * P.ws.nslots;
+  const float* pl = reinterpret_cast<const float*>(P.ws_base + P.ws.part_l) + ((size_t)bh * 64 + r) * P.ws.nslots;
+  float M = kNegInf;
+  #pragma unroll 8
+  for (int s = q; s < nslots_used; s += 4) M = fmaxf(M, get_c(pm + s));
+  M = fmaxf(M, __shfl_xor(M, 1));
+  M = fmaxf(M, __shfl_xor(M, 2));
+  float S = 0.f;
+  if (M != kNegInf) {
+    #pragma unroll 8
+    for (int s = q; s < nslots_used; s += 4) S += get_c(pl + s) * fast_exp2(get_c(pm + s) - M);
+  }
+  S += __shfl_xor(S, 1);
+  S += __shfl_xor(S, 2);
+  if (q == 0) {
+    float* l2 = reinterpret_cast<float*>(P.ws_base + P.ws.lse2) + (size_t)bh * 64;
+    // rows without any key (r >= L) get +inf so that their probabilities are 0
+    put_c(l2 + r, (S > 0.f) ? M + __log2f(S) : __builtin_huge_valf());
+  }
+}
+
+// The work order of the fused proxy launch, built on the host from the head
+// table.  Tasks are (batch b, VS head v, key range); idx = b * nvs * nwg +
+// first[v] * nwg + range * cnt[v] + (v - first[v]) lists the VS heads of one
+// KV group range by range, so they read the same keys one after another.
+// Ticket t (the order in which work-groups start) maps to pass 1 task t for
+// t < D, then alternates pass 1 task D + k and pass 2 task k, then the last
+// pass 2 tasks.  D >= (largest group) * nwg, so a pass 2 task starts after
+// every pass 1 task of its head has started.
+struct VsFusedMeta {
+  int32_t* sync;        // [0] ticket, [1 + i] pass 1 tasks done, [1 + BV + i] LSE ready (i = b * nvs + v)
+  int32_t nvs, nwg, T, D;
+  uint8_t head[MINF_MAX_HEADS];    // VS heads in ascending order
+  uint8_t first[MINF_MAX_HEADS];   // per VS index: first VS index of its KV group
+  uint8_t cnt[MINF_MAX_HEADS];     // per VS index: VS heads in its KV group
+};
+
+// Polls of a pass 2 task for its head's LSE (about a second): the work order
+// makes the wait end (every pass 1 task it waits for started earlier and
+// waits for nothing), the bound only keeps a broken order from hanging.
+constexpr int kVsWaitPolls = 1 << 22;
+
+// The whole proxy in one launch: pass 1 of a head's key ranges, the LSE fold
+// by the last of them to finish, and pass 2, which waits (bounded) for that
+// head's LSE.  With the order above, the pass 2 reads of a KV group's keys
+// follow its pass 1 reads closely, while they are still in the on-die cache.
+template <typename T, int DH>
+__global__ __launch_bounds__(256) void vs_fused_kernel(VsParams P, VsFusedMeta M) {
+  __shared__ float ptile[4][64][33];
+  __shared__ float red[2][4][64];
+  __shared__ float dacc[4][kVsWaveKeys];
+  __shared__ int s_val;
+  if (threadIdx.x == 0) s_val = __hip_atomic_fetch_add(M.sync, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  __syncthreads();
+  const int t = s_val;
+  __syncthreads();
+  const int NT = M.T, D = M.D, mid = NT - D;
+  int pass, idx;
+  if (t < D) { pass = 1; idx = t; }
+  else if (t - D < 2 * mid) {
+    const int k = t - D;
+    pass = (k & 1) ? 2 : 1;
+    idx = (k & 1) ? (k >> 1) : D + (k >> 1);
+  } else { pass = 2; idx = t - D - mid; }
+  if (idx >= NT) return;
+  const int per_b = M.nvs * M.nwg;
+  const int b = idx / per_b, rem = idx - b * per_b;
+  const int v0 = rem / M.nwg;
+  const int f = M.first[v0], c = M.cnt[v0];
+  const int local = rem - f * M.nwg;
+  const int range = local / c, v = f + (local - range * c);
+  const int bh = b * P.Hq + M.head[v];
+  const int hv = b * M.nvs + v;
+  int32_t* done = M.sync + 1;
+  int32_t* ready = M.sync + 1 + P.B * M.nvs;
+  const int wave = threadIdx.x >> 6;
+  if (pass == 1) {
+    fused_task<T, DH, 1>(P, bh, range, ptile[wave], red, dacc[wave]);
+    drain();
+    __syncthreads();
+    if (threadIdx.x == 0)
+      s_val = __hip_atomic_fetch_add(done + hv, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == M.nwg - 1;
+    __syncthreads();
+    if (s_val) {
+      fused_fold(P, bh, M.nwg);
+      drain();
+      __syncthreads();
+      if (threadIdx.x == 0) __hip_atomic_store(ready + hv, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+  } else {
+    if (threadIdx.x == 0) {
+      int ok = 0;
+      for (int i = 0; i < kVsWaitPolls; ++i) {
+        if (__hip_atomic_load(ready + hv, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) { ok = 1; break; }
+        __builtin_amdgcn_s_sleep(8);
+      }
+      s_val = ok;
+    }
+    __syncthreads();
+    if (!s_val) return;
+    fused_task<T, DH, 2>(P, bh, range, ptile[wave], red, dacc[wave]);
+  }
+}
+
 // Top-v columns / top-s offsets (selection order: score descending, index
 // ascending; outputs ascending), the same radix select as topk.h spread over
 // kTopkSeg-element segments of each array: array a = 2 * bh + which (which
@@ -516,14 +865,8 @@ __global__ __launch_bounds__(256) void vs_tk_write_kernel(VsParams P) {
     for (int i = t.k + tid; i < t.cap; i += 256) t.out[i] = -1;
 }
 
-template <typename T, int DH>
-hipError_t launch_t(const VsParams& p, hipStream_t st) {
+hipError_t launch_topk(const VsParams& p, hipStream_t st) {
   const unsigned BH = (unsigned)(p.B * p.Hq);
-  const unsigned nwg = (unsigned)((p.n + kVsGroupKeys - 1) / kVsGroupKeys);
-  hipLaunchKernelGGL((vs_proxy_kernel<T, DH, 1>), dim3(nwg, BH), dim3(256), 0, st, p);
-  hipLaunchKernelGGL(vs_lse_kernel, dim3(16, BH), dim3(256), 0, st, p, (int)(nwg * 4));
-  hipLaunchKernelGGL((vs_proxy_kernel<T, DH, 2>), dim3(nwg, BH), dim3(256), 0, st, p);
-  hipLaunchKernelGGL(vs_diag_kernel, dim3((p.n + 255) / 256, BH), dim3(256), 0, st, p);
   const dim3 tkg((unsigned)p.ws.tk_segs, 2 * BH);
   hipLaunchKernelGGL(vs_tk_init_kernel, dim3(2 * BH), dim3(64), 0, st, p);
   for (int shift = 24; shift >= 0; shift -= 8) {
@@ -535,11 +878,53 @@ hipError_t launch_t(const VsParams& p, hipStream_t st) {
   return hipGetLastError();
 }
 
+template <typename T, int DH>
+hipError_t launch_t(const VsParams& p, hipStream_t st) {
+  const unsigned BH = (unsigned)(p.B * p.Hq);
+  const unsigned nwg = (unsigned)((p.n + kVsGroupKeys - 1) / kVsGroupKeys);
+  hipLaunchKernelGGL((vs_proxy_kernel<T, DH, 1>), dim3(nwg, BH), dim3(256), 0, st, p);
+  hipLaunchKernelGGL(vs_lse_kernel, dim3(16, BH), dim3(256), 0, st, p, (int)(nwg * 4));
+  hipLaunchKernelGGL((vs_proxy_kernel<T, DH, 2>), dim3(nwg, BH), dim3(256), 0, st, p);
+  hipLaunchKernelGGL(vs_diag_kernel, dim3((p.n + 255) / 256, BH), dim3(256), 0, st, p);
+  return launch_topk(p, st);
+}
+
+template <typename T, int DH>
+hipError_t launch_fused_t(const VsParams& p, hipStream_t st) {
+  VsFusedMeta m{};
+  const int gsz = p.Hq / p.Hkv;
+  int gmax = 0;
+  for (int h = 0; h < p.Hq; ++h)
+    if (p.ht.kind[h] == MINF_VSLASH) m.head[m.nvs++] = (uint8_t)h;
+  for (int v = 0; v < m.nvs;) {
+    int e = v;
+    while (e < m.nvs && m.head[e] / gsz == m.head[v] / gsz) ++e;
+    for (int u = v; u < e; ++u) { m.first[u] = (uint8_t)v; m.cnt[u] = (uint8_t)(e - v); }
+    gmax = std::max(gmax, e - v);
+    v = e;
+  }
+  m.nwg = (p.n + kVsGroupKeys - 1) / kVsGroupKeys;
+  m.T = p.B * m.nvs * m.nwg;
+  m.D = std::min(m.T, (gmax + 1) * m.nwg);
+  m.sync = reinterpret_cast<int32_t*>(p.ws_base + p.ws.sync);
+  if (m.T > 0) {
+    const hipError_t e = launch_fill_i32(m.sync, 1 + 2 * (int64_t)p.B * m.nvs, 0, st);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((vs_fused_kernel<T, DH>), dim3((unsigned)(2 * m.T)), dim3(256), 0, st, p, m);
+  }
+  return launch_topk(p, st);
+}
+
 }  // namespace
 
 hipError_t launch_vs_index(const VsParams& p, hipStream_t st) {
   if (p.in_bf16) return p.dh == 128 ? launch_t<uint16_t, 128>(p, st) : launch_t<uint16_t, 64>(p, st);
   return p.dh == 128 ? launch_t<float, 128>(p, st) : launch_t<float, 64>(p, st);
+}
+
+hipError_t launch_vs_index_fused(const VsParams& p, hipStream_t st) {
+  if (p.in_bf16) return p.dh == 128 ? launch_fused_t<uint16_t, 128>(p, st) : launch_fused_t<uint16_t, 64>(p, st);
+  return p.dh == 128 ? launch_fused_t<float, 128>(p, st) : launch_fused_t<float, 64>(p, st);
 }
 
 }  // namespace minf
