@@ -36,9 +36,9 @@ PEAK_HBM_GBS = 8000.0            # MI355X HBM3E
 ATTN_KERNEL = "attn_bf16_d128_kernel"
 ATTN_SOURCES = ["long_context_prefill_amd/csrc/attn_bf16.hip", "long_context_prefill_amd/csrc/common.h",
                 "long_context_prefill_amd/csrc/kernels.h", "include/minf.h"]
-ATTN_TRAFFIC = {"workload": "n128k_h32kv8_d128_bf16_mixed", "sources": "28e3785b4fe3bb3a",
-                "fetch_kib": 20853949.08, "fetch_factor": 1048576 / 524304.54,
-                "write_kib": 2108084.08, "write_factor": 1048576 / 1048576.0}
+ATTN_TRAFFIC = {"workload": "n128k_h32kv8_d128_bf16_mixed", "sources": "2685d371d3ac21ff",
+                "fetch_kib": 20613534.04, "fetch_factor": 1048576 / 524305.96,
+                "write_kib": 2107844.41, "write_factor": 1048576 / 1048576.0}
 
 
 def log(*a):
@@ -395,6 +395,8 @@ def main():
     ap.add_argument("--no-exact", action="store_true", help="skip the exact slash pairs (slash_tile=1) layer")
     ap.add_argument("--no-search", action="store_true", help="skip the pattern search summary (32K calibration layer)")
     ap.add_argument("--no-ragged", action="store_true", help="skip the ragged batch summary")
+    ap.add_argument("--no-vs-single", action="store_true",
+                    help="skip timing the Vertical-Slash estimate alone (two-launch vs single-launch proxy)")
     ap.add_argument("--search", type=int, default=0,
                     help="only run the offline pattern search on a calibration layer of this length")
     ap.add_argument("--search-eps", type=float, default=0.05, help="error bound of the pattern search")
@@ -534,7 +536,7 @@ def main():
         log(f"exact slash pairs in {time.time() - t0:.1f}s")
 
     vs_fused = None
-    if "vslash" in per_kind:
+    if "vslash" in per_kind and not a.no_vs_single:
         # the Vertical-Slash estimate alone, warm: the two-launch path the layer
         # uses against the single-launch proxy (minf_vs_index_fused)
         def vs_ms(fn, reps=20):
