@@ -204,3 +204,44 @@ def test_full_size_exact_slash_pairs():
     ref = _row_refs(q, _Widened(k), _Widened(v), rows, lambda i: O.vs_row_keys(i, cols, cover, 1), sc,
                     f"head {h} exact pairs")
     U.compare_output(og, ref, p.dtype, f"128K head {h} exact pairs, {len(rows)} rows")
+
+
+@pytest.mark.timeout(400)
+def test_full_size_single_launch_vs_index():
+    """minf_vs_index_fused at the 128K mixed layer, in the launch the bench
+    times: the selections of VS heads from two KV groups against the oracle's
+    proxy scores, and every VS head's scores against the two-launch path."""
+    import torch
+    t0 = time.time()
+    p = gen.make_workload(3)
+    U.log(f"workload {p.name}: generated in {time.time() - t0:.0f}s")
+    g = p.Hq // p.Hkv
+    prob = M.make_problem(p.B, p.Hq, p.Hkv, p.n, p.dh, p.dtype, "f32", p.scale)
+    heads = M.make_heads(p.heads)
+    buf = M.alloc_buffers(prob, heads)
+    Q, K, _ = U.device_inputs(p)
+    scores = []
+    for fn in (M.minf_vs_index_fused, M.minf_vs_index):
+        c = torch.zeros((p.B, p.Hq, p.n), dtype=torch.float32, device="cuda")
+        r = torch.zeros_like(c)
+        fn(prob, heads, Q, K, buf["vert_idx"], buf["slash_idx"], c, r, buf["ws"])
+        torch.cuda.synchronize()
+        if not scores:
+            vi, si = buf["vert_idx"].cpu().numpy(), buf["slash_idx"].cpu().numpy()
+        scores.append((c.cpu().numpy(), r.cpu().numpy()))
+    del Q, K
+    vs_heads = [h for h, c in enumerate(p.heads) if c.kind == gen.VSLASH]
+    assert vs_heads
+    for h in vs_heads:
+        for x, y, what in ((scores[0][0], scores[1][0], "columns"), (scores[0][1], scores[1][1], "offsets")):
+            s = max(float(np.abs(y[0, h]).max()), 1e-30)
+            assert np.abs(x[0, h] - y[0, h]).max() <= 1e-5 * s, (h, what)
+    checked = [vs_heads[0]] + [h for h in vs_heads if h // g != vs_heads[0] // g][:1]
+    for h in checked:
+        cfg = p.heads[h]
+        q = _f32(p.Q[0, h], p.dtype).astype(np.float64)
+        k = _f32(p.K[0, h // g], p.dtype).astype(np.float64)
+        c, r = O.vs_proxy_scores(q, k, cfg.last_q, p.eff_scale)
+        d1, _ = U.check_selection(vi[0, h][vi[0, h] >= 0], c, cfg.n_vertical, f"head {h} columns")
+        d2, _ = U.check_selection(si[0, h][si[0, h] >= 0], r, cfg.n_slash, f"head {h} offsets")
+        U.log(f"  head {h}: single-launch selection matches ({d1 + d2} near-tie differences, {time.time() - t0:.0f}s)")
