@@ -76,3 +76,26 @@ def test_fused_proxy_is_deterministic():
     assert np.array_equal(c1, c2) and np.array_equal(r1, r2)
     for k in ("vert_idx", "slash_idx"):
         assert np.array_equal(b1[k].cpu().numpy(), b2[k].cpu().numpy())
+
+
+@pytest.mark.parametrize("Hkv,B", [(4, 3), (1, 2)])
+def test_fused_proxy_wide_groups(Hkv, B):
+    """Up to 64 VS heads in one KV group (the work order's per-group tables),
+    VS heads scattered among other kinds, several batches, ragged n: against
+    the oracle and the two-launch path."""
+    from synth import gen
+    U.log(f"wide groups Hkv={Hkv} B={B}")
+    kinds = [gen.vslash(64, 30, 50), gen.vslash(20, 8, 100), gen.ashape(4, 32), gen.vslash(64, 200, 8)]
+    heads = [kinds[h % 4] for h in range(64)]
+    p = gen.make_small(n=700, B=B, Hq=64, Hkv=Hkv, dh=64, seed=53 + Hkv, heads=heads)
+    res = O.run_layer(p.Q, p.K, p.V, p.dtype, p.heads, scale=p.scale, attend=False)
+    buf, c1, r1 = _run(p, fused=True)
+    check_index(p, res, buf, c1, r1)
+    _, c2, r2 = _run(p, fused=False)
+    for b in range(B):
+        for h, cfg in enumerate(heads):
+            if cfg.kind != O.VSLASH:
+                continue
+            for x, y in ((c1, c2), (r1, r2)):
+                s = max(float(np.abs(y[b, h]).max()), 1e-30)
+                assert np.abs(x[b, h] - y[b, h]).max() <= 1e-5 * s, (b, h)
