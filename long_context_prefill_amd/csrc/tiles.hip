@@ -34,21 +34,28 @@ __device__ __forceinline__ int64_t ashape_edges(int64_t n, int64_t g, int64_t w)
 }
 
 // Block-wide exclusive scan of one int per thread (256 threads), returns the
-// total through *total.
+// total through *total: an inclusive scan inside each wave by shuffles, then
+// the four wave totals through LDS (two barriers; sh holds 4 ints).
 __device__ int block_exscan(int x, int* sh, int* total) {
-  const int t = threadIdx.x;
-  sh[t] = x;
-  __syncthreads();
-  for (int off = 1; off < 256; off <<= 1) {
-    int y = t >= off ? sh[t - off] : 0;
-    __syncthreads();
-    sh[t] += y;
-    __syncthreads();
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  int v = x;
+  #pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int y = __shfl_up(v, off);
+    if (lane >= off) v += y;
   }
-  const int incl = sh[t];
-  *total = sh[255];
+  if (lane == 63) sh[w] = v;
   __syncthreads();
-  return incl - x;
+  int before = 0, tot = 0;
+  #pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int t = sh[i];
+    before += i < w ? t : 0;
+    tot += t;
+  }
+  *total = tot;
+  __syncthreads();     // sh is reused by the next call
+  return before + v - x;
 }
 
 // 1) validate indices, initialise kept_edges, merge slash ranges.
