@@ -194,8 +194,12 @@ minf_status minf_vs_index(const minf_problem* prob, const minf_head_cfg* heads,
  * head's LSE.  Arguments, outputs, workspace and errors as minf_vs_index;
  * scores equal minf_vs_index's up to the summation order of the LSE and slash
  * sums, so selections can differ only between near-equal scores.  The
- * two-launch minf_vs_index is faster on MI355X and remains the path that
- * minf_prefill_ragged and the layer use. */
+ * waits end by construction (a second-pass work-group waits only for work
+ * that started before it and waits for nothing); each is still bounded (about
+ * a second), and a wait that ran out would leave its key range's column and
+ * slash scores NaN rather than unwritten.  The two-launch minf_vs_index is
+ * faster on MI355X and remains the path that minf_prefill_ragged and the
+ * layer use. */
 minf_status minf_vs_index_fused(const minf_problem* prob, const minf_head_cfg* heads,
                                 const void* Q, const void* K,
                                 int32_t* vert_idx, int32_t* slash_idx,
