@@ -55,7 +55,7 @@ struct AttnParams {
 // kMinRun blocks, so that the work-groups running together on one XCD
 // (4 per CU, 32 CUs) mostly work on neighbouring blocks of one head; and at
 // most kMaxUnits units in all.
-constexpr int kUnitsPerGroup = 32;
+constexpr int kUnitsPerGroup = 16;
 constexpr int kMinRun = 128;
 constexpr int kMaxUnits = 4096;
 inline void attn_sched_shape(int B, int Hq, int Hkv, int64_t nq, int* P, int* R) {
