@@ -186,9 +186,10 @@ minf_status minf_vs_index(const minf_problem* prob, const minf_head_cfg* heads,
                           float* vert_score, float* slash_score,
                           void* ws, size_t ws_bytes, void* stream);
 
-/* The same Vertical-Slash estimation with the proxy in one launch (the
- * conclusion of the cost-model page on the index stage: fewer read and write
- * rounds and synchronisations between the reduce and the selection): the
+/* The same Vertical-Slash estimation with the proxy in one launch (MInference
+ * page, section 3.1: on a GPU the index cost is counted in read and write
+ * rounds and synchronisations, so fusing the reduce with the selection
+ * matters): the
  * per-row LSE fold and the column and slash sums run in the same grid as the
  * proxy scores, a work-group of the second pass waiting (bounded) for its
  * head's LSE.  Arguments, outputs, workspace and errors as minf_vs_index;

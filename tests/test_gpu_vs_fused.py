@@ -1,8 +1,7 @@
 """GPU checks of minf_vs_index_fused, the Vertical-Slash proxy in one launch
-(cost-model page, the conclusion on the index stage: fewer read and write
-rounds and synchronisations between the reduce and the selection; the
-estimate itself follows the MInference page, section 6.2, and the blog,
-section 2.3.2):
+(MInference page, section 3.1: on a GPU the index cost is counted in read
+and write rounds and synchronisations; the estimate itself follows the
+MInference page, section 6.2, and the blog, section 2.3.2):
 
 * column and slash scores and the selections against the oracle, on the
   same cases as the two-launch path (several key ranges, ragged tails, GQA,
