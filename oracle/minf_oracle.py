@@ -6,7 +6,9 @@ product path (the HIP library and its Python binding) never touches it and
 shares no code with it.
 
 Everything here is a plain, slow, step-by-step restatement of what the pages
-define, in float64 NumPy.  Sources (cited by page title and section):
+define, in float64 NumPy; the restricted softmax over explicit key ranges for
+long sequences is plain C in double precision (oracle/attend.c, compiled by
+build_c()).  Sources (cited by page title and section):
 
 * [MInf]  PaperTrace 2.1.2 "MInference: 按 head 模式加速长上下文 Prefill"
 * [Blog]  blog-zz7 "LLM模型之MInference", section 2.3
@@ -216,13 +218,19 @@ def vs_mask(rows: np.ndarray, nkeys: int, n: int, cols, offs, slash_tile: int,
     t = slash_tile
     if cover is None:
         cover = slash_offset_set(offs, n, t)
+    rows = np.asarray(rows, dtype=np.int64)
     i = rows[:, None]
     j = np.arange(nkeys)[None, :]
-    x = t * (rows[:, None] // t) - j              # offset of key j from block start
-    idx = x + t - 1
-    ok = (idx >= 0) & (idx < cover.shape[0])
-    covered = np.zeros(idx.shape, dtype=bool)
-    covered[ok] = cover[idx[ok]]
+    # Key j of row i's block u is covered iff cover[t*u - j + t - 1] (the
+    # offset x = t*u - j, stored at x + t - 1).  Read along j, that is the
+    # array `cover` backwards from position t*u + t - 1; with `rev` the
+    # reversed array (followed by zeros for x < -(t-1), i.e. keys past the
+    # block), cover[t*u + t - 1 - j] = rev[L - t - t*u + j], L = len(cover).
+    L = cover.shape[0]
+    rev = np.zeros(L + nkeys, dtype=bool)
+    rev[:L] = cover[::-1]
+    start = L - t - t * (rows // t)               # >= 0: t*u <= i <= n - 1 = L - t
+    covered = np.lib.stride_tricks.sliding_window_view(rev, nkeys)[start]
     colset = np.zeros(nkeys, dtype=bool)
     cc = np.asarray(cols, dtype=np.int64)
     colset[cc[cc < nkeys]] = True
@@ -324,6 +332,123 @@ def attend_row_keys(q_i: np.ndarray, k: np.ndarray, v: np.ndarray, keys: np.ndar
     p = np.exp(s - m)
     l = p.sum()
     return (p @ v[keys]) / l, m + math.log(l)
+
+
+# ----------------------------------------------------------------------------
+# row by row over key ranges, in C (oracle/attend.c): the same restricted
+# softmax for long sequences, where a row keeps few of the keys before it.
+# N(i) is listed as disjoint inclusive key ranges; the ranges below are the
+# sets of Eq. 3, of the slash expansion / Eq. 5 and of Eq. 6.
+# ----------------------------------------------------------------------------
+
+_CLIB = None
+_C_SRC = os.path.join(os.path.dirname(os.path.abspath(__file__)), "attend.c")
+_C_LIB = os.path.join(os.path.dirname(os.path.abspath(__file__)), "liboracle.so")
+
+
+def build_c(force: bool = False) -> str:
+    """Compile oracle/attend.c into oracle/liboracle.so with the host C
+    compiler (plain -O2, IEEE arithmetic)."""
+    import subprocess
+    if force or not os.path.exists(_C_LIB) or os.path.getmtime(_C_LIB) < os.path.getmtime(_C_SRC):
+        tmp = _C_LIB + f".tmp{os.getpid()}"
+        subprocess.run(["gcc", "-O2", "-fPIC", "-shared", _C_SRC, "-o", tmp, "-lm"], check=True)
+        os.replace(tmp, _C_LIB)
+    return _C_LIB
+
+
+def _clib():
+    global _CLIB
+    if _CLIB is None:
+        import ctypes
+        lib = ctypes.CDLL(build_c())
+        f = lib.oracle_attend_ranges
+        P = ctypes.c_void_p
+        f.argtypes = [ctypes.c_int64, ctypes.c_int64, P, P, P, P, P, P, ctypes.c_double, P, P]
+        f.restype = ctypes.c_int
+        _CLIB = lib
+    return _CLIB
+
+
+def ashape_row_ranges(i: int, sink: int, window: int):
+    """N(i) of Eq. 3 as disjoint ranges: the sinks [0, min(g-1, i)] and the
+    part of the window [max(0, i-w+1), i] that lies past them."""
+    lo, hi = [], []
+    a = min(sink - 1, i)
+    if a >= 0:
+        lo.append(0)
+        hi.append(a)
+    b = max(sink, i - window + 1, 0)
+    if window > 0 and b <= i:
+        lo.append(b)
+        hi.append(i)
+    return np.array(lo, dtype=np.int64), np.array(hi, dtype=np.int64)
+
+
+def bs_row_ranges(i: int, J: Sequence[np.ndarray], block: int = BLOCK):
+    """N(i) of Eq. 6 as ranges: each selected block of row i's query block,
+    cut at the row (causal)."""
+    v = np.sort(np.asarray(J[i // block], dtype=np.int64))
+    lo = v * block
+    hi = np.minimum(lo + block - 1, i)
+    keep = lo <= hi
+    return lo[keep], hi[keep]
+
+
+def span_runs(cover: np.ndarray, slash_tile: int):
+    """The covered offsets x (cover from slash_offset_set, indexed x + t - 1)
+    as sorted disjoint inclusive runs [a, b]."""
+    d = np.diff(np.concatenate([[0], cover.astype(np.int8), [0]]))
+    a = np.flatnonzero(d == 1)
+    b = np.flatnonzero(d == -1) - 1
+    return a - (slash_tile - 1), b - (slash_tile - 1)
+
+
+def vs_row_ranges(i: int, cols, cover: np.ndarray, slash_tile: int, runs=None):
+    """N(i) of the VS set as disjoint ranges: for row i's query block
+    u = i // t, the keys j = t*u - x of every covered run of offsets x,
+    clipped to [0, i], then each column j <= i that no slash of block u
+    covers, as a range of one key."""
+    t = slash_tile
+    xa, xb = span_runs(cover, t) if runs is None else runs
+    u = i // t
+    lo = np.maximum(t * u - xb, 0)
+    hi = np.minimum(t * u - xa, i)
+    keep = lo <= hi
+    c = np.asarray(cols, dtype=np.int64)
+    c = c[c <= i]
+    unc = c[~cover[t * u - c + t - 1]]
+    return np.concatenate([lo[keep], unc]), np.concatenate([hi[keep], unc])
+
+
+def attend_rows_ranges(q_rows: np.ndarray, k: np.ndarray, v: np.ndarray, rows: np.ndarray,
+                       ranges_fn: Callable, scale: float):
+    """o_i and LSE_i for the given rows over N(i) = ranges_fn(i) (disjoint
+    inclusive key ranges), in double precision (attend.c).  q_rows [R, dh]
+    are rows `rows` of Q; k, v [n, dh]; all float32 values (bf16 widens to
+    float32 exactly).  Empty rows give o = 0 and LSE = -inf."""
+    rows = np.asarray(rows, dtype=np.int64)
+    R, dh = rows.shape[0], k.shape[1]
+    los, his, ptr = [], [], [0]
+    for i in rows:
+        lo, hi = ranges_fn(int(i))
+        los.append(lo)
+        his.append(hi)
+        ptr.append(ptr[-1] + lo.shape[0])
+    lo = np.ascontiguousarray(np.concatenate(los) if los else np.zeros(0), dtype=np.int64)
+    hi = np.ascontiguousarray(np.concatenate(his) if his else np.zeros(0), dtype=np.int64)
+    ptr = np.asarray(ptr, dtype=np.int64)
+    assert np.all(lo >= 0) and np.all(hi < k.shape[0]) and np.all(hi <= np.repeat(rows, np.diff(ptr)))
+    q = np.ascontiguousarray(q_rows, dtype=np.float32)
+    kk = np.ascontiguousarray(k, dtype=np.float32)
+    vv = np.ascontiguousarray(v, dtype=np.float32)
+    o = np.zeros((R, dh))
+    lse = np.zeros(R)
+    rc = _clib().oracle_attend_ranges(R, dh, q.ctypes.data, kk.ctypes.data, vv.ctypes.data, ptr.ctypes.data,
+                                      lo.ctypes.data, hi.ctypes.data, float(scale), o.ctypes.data, lse.ctypes.data)
+    if rc != 0:
+        raise MemoryError("oracle_attend_ranges: out of memory")
+    return o, lse
 
 
 # ----------------------------------------------------------------------------
