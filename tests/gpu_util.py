@@ -59,6 +59,73 @@ def load_oracle_indices(p, res, buf):
     buf["blk_cnt"].copy_(torch.from_numpy(bc).to(dev))
 
 
+def gpu_given(p, buf, heads=None):
+    """The GPU's own index sets in the form O.run_layer(given=...) takes:
+    {(b, h): (cols, offs)} for Vertical-Slash heads and {(b, h): [J_u]} for
+    Block-Sparse heads (the comparison protocol runs the oracle's attention
+    on the GPU's index sets)."""
+    vi = buf["vert_idx"].cpu().numpy()
+    si = buf["slash_idx"].cpu().numpy()
+    bi = buf["blk_idx"].cpu().numpy()
+    bc = buf["blk_cnt"].cpu().numpy()
+    out = {}
+    for b in range(p.B):
+        for h in (range(p.Hq) if heads is None else heads):
+            kind = p.heads[h].kind
+            if kind == O.VSLASH:
+                out[(b, h)] = (vi[b, h][vi[b, h] >= 0].astype(np.int64), si[b, h][si[b, h] >= 0].astype(np.int64))
+            elif kind == O.BSPARSE:
+                out[(b, h)] = [bi[b, h, u, :bc[b, h, u]].astype(np.int64) for u in range(bi.shape[2])]
+    return out
+
+
+def check_block_selections(J, cnt, scores, k, force, what):
+    """Every query block's Block-Sparse selection against the oracle's block
+    scores at once, with the rule of check_selection: the GPU set of row u
+    (J[u, :cnt[u]]) may differ from the oracle's top-min(k, u+1) set (score
+    descending, index ascending) only in blocks whose oracle score lies within
+    1e-4 relative of the row's threshold t_u, the k-th largest score.
+    scores [nq, nq] fp64 (entries above the diagonal are ignored); forced
+    blocks score +inf, so a row whose threshold is infinite must match
+    exactly.  Returns (differing selections, exempt near-ties)."""
+    nq = scores.shape[0]
+    u = np.arange(nq)
+    causal = np.arange(nq)[None, :] <= u[:, None]
+    s = np.where(causal, np.asarray(scores, dtype=np.float64), -np.inf)
+    if force & O.FORCE_FIRST_BLOCK:
+        s[:, 0] = np.inf
+    if force & O.FORCE_DIAG_BLOCK:
+        s[u, u] = np.inf
+    kk = np.minimum(int(k), u + 1)
+    assert np.array_equal(np.asarray(cnt[:nq], dtype=np.int64), kk), f"{what}: block counts"
+    width = J.shape[1]
+    valid = np.arange(width)[None, :] < kk[:, None]
+    Jv = np.where(valid, J[:nq, :width], 0).astype(np.int64)
+    assert np.all((Jv >= 0) & (Jv <= u[:, None])), f"{what}: a block outside [0, u]"
+    d = np.diff(np.where(valid, Jv, np.iinfo(np.int64).max), axis=1)
+    assert np.all(d[valid[:, 1:]] > 0), f"{what}: blocks not strictly ascending"
+    sel = np.zeros((nq, nq), dtype=bool)
+    sel[np.repeat(u, width)[valid.ravel()], Jv[valid]] = True
+    # t_u: the kk[u]-th largest score of row u (the smallest causal score when
+    # the whole row is taken)
+    kmax = int(kk.max())
+    part = -np.partition(-s, kmax - 1, axis=1)[:, :kmax]
+    t = np.sort(part, axis=1)[:, ::-1][u, kk - 1]
+    # the oracle's set: every score above t, then the lowest-indexed ties
+    gt = s > t[:, None]
+    eq = (s == t[:, None]) & causal
+    need = kk - gt.sum(axis=1)
+    ref = gt | (eq & (np.cumsum(eq, axis=1) <= need[:, None]))
+    diff = ref ^ sel
+    with np.errstate(invalid="ignore"):
+        near = np.abs(s - t[:, None]) <= NEAR_TIE_REL * np.abs(t)[:, None]
+    bad = diff & ~near
+    assert not bad.any(), (f"{what}: block rows {np.nonzero(bad.any(axis=1))[0][:8].tolist()} "
+                           f"differ beyond the near-tie band")
+    nd = int(diff.sum())
+    return nd, nd
+
+
 def compare_output(O_gpu, O_ref, dtype, what=""):
     """Element-wise comparison to the benchmark spec's tolerances."""
     d = np.abs(np.asarray(O_gpu, dtype=np.float64) - O_ref)

@@ -2,18 +2,28 @@
 configuration bench.py times (whole layer: Vertical-Slash index,
 Block-Sparse index, tile build, sparse attention, fp32 output).
 
-For every workload, one head of each pattern kind present is checked:
+For every workload and EVERY head:
 * its index against the oracle's: Vertical-Slash columns and offsets, and
   every query block's Block-Sparse selection, identical except candidates
   whose oracle score lies within 1e-4 relative of the k-th threshold;
-* its kept edges, exactly, from the GPU's own index sets;
+* its kept edges, exactly, against the oracle's count over the GPU's own
+  index sets;
 * its output rows against the oracle's restricted softmax over the GPU's own
   index sets (max-abs 1e-2, mean-abs 1e-3 for bf16 inputs): all rows up to
   32K tokens; above that the 4096 seeded sampled rows plus the edge rows
-  for the first checked head and 512 of them for the others.
+  {0, 1, 63, 64, 65, n/2, n-65, n-64, n-1}.
+The oracle runs on a pool of threads, one KV group at a time (its four
+query heads share the widened K and V), each head's rows split over
+several tasks.  Every row of a sequence up to 32K tokens is checked with
+masked dense products of row chunks (O.attend_rows); the sampled rows of the
+longer sequences row by row over their candidate key ranges
+(O.attend_rows_ranges, plain C in double precision), which costs what the
+row keeps rather than the whole prefix.
 """
 import math
+import os
 import time
+from concurrent.futures import ThreadPoolExecutor
 
 import numpy as np
 import pytest
@@ -29,15 +39,12 @@ from oracle import minf_oracle as O  # noqa: E402
 from synth import gen  # noqa: E402
 
 
-def _checked_heads(p):
-    seen, out = set(), []
-    for h, c in enumerate(p.heads):
-        if c.kind not in seen:
-            seen.add(c.kind)
-            out.append(h)
-    if len(out) == 1:
-        out.append(p.Hq - 1)          # a second head from another KV group
-    return out
+def _threads():
+    try:
+        c = len(os.sched_getaffinity(0))
+    except AttributeError:
+        c = os.cpu_count() or 1
+    return max(1, min(16, c))
 
 
 def _f32(x, dtype):
@@ -48,7 +55,6 @@ def _f32(x, dtype):
 
 def _row_refs(q, k, v, rows, keys_fn, scale, what):
     """Oracle rows (float64 arithmetic on exactly widened inputs), on threads."""
-    from concurrent.futures import ThreadPoolExecutor
 
     def one(i):
         keys = keys_fn(int(i))
@@ -56,7 +62,7 @@ def _row_refs(q, k, v, rows, keys_fn, scale, what):
 
     out = np.zeros((len(rows), v.shape[1]))
     t0 = time.time()
-    with ThreadPoolExecutor(12) as ex:
+    with ThreadPoolExecutor(_threads()) as ex:
         for t, (o, _) in enumerate(ex.map(one, rows)):
             out[t] = o
             if t % 512 == 511:
@@ -78,14 +84,94 @@ class _Widened:
         return self.a.shape
 
 
-@pytest.mark.timeout(400)
+def _check_index(p, given, cnt, h, k64):
+    """Head h's GPU selections against the oracle's estimate (k64: its KV
+    head's keys in float64); returns the number of (exempt) differences."""
+    cfg = p.heads[h]
+    q = _Widened(_f32(p.Q[0, h], p.dtype))
+    if cfg.kind == gen.VSLASH:
+        c, r = O.vs_proxy_scores(q, k64, cfg.last_q, p.eff_scale)
+        cols, offs = given[(0, h)]
+        d1, _ = U.check_selection(cols, c, cfg.n_vertical, f"head {h} columns")
+        d2, _ = U.check_selection(offs, r, cfg.n_slash, f"head {h} offsets")
+        return d1 + d2
+    if cfg.kind == gen.BSPARSE:
+        scores = O.bs_block_scores(q, k64, p.eff_scale)
+        J = given[(0, h)]
+        Jm = np.full((len(J), max(1, max(len(x) for x in J))), -1, dtype=np.int64)
+        for u, x in enumerate(J):
+            Jm[u, :len(x)] = x
+        return U.check_block_selections(Jm, cnt[0, h], scores, cfg.topk_blocks, cfg.force_flags, f"head {h}")[0]
+    return 0
+
+
+def _check_group(p, kv, rows, given, cnt, ke, ref, nt):
+    """KV group kv's query heads: each head's index against the oracle's
+    estimate, its kept edges (ke) against the oracle's count over the GPU's
+    index sets (given, cnt), and the oracle's output rows over those sets
+    into ref[h].  Returns the number of exempt near-tie differences."""
+    from threadpoolctl import threadpool_limits
+    n, g, sc = p.n, p.Hq // p.Hkv, p.eff_scale
+    parts = max(1, nt // g)
+    k64 = O.widen(p.K[0, kv], p.dtype)
+    hs = list(range(kv * g, (kv + 1) * g))
+    res = {h: O.head_index(None, None, p.heads[h], n, sc, 64, O.BLOCK, given.get((0, h))) for h in hs}
+    sampled = p.rows is not None
+    if sampled:
+        # sampled rows of a long sequence: row by row over the listed key
+        # ranges, in C (a row keeps a small share of the keys before it)
+        k32, v32 = _f32(p.K[0, kv], p.dtype), _f32(p.V[0, kv], p.dtype)
+        fns = {}
+        for h in hs:
+            cfg, r = p.heads[h], res[h]
+            if r.kind == O.ASHAPE:
+                fns[h] = lambda i, cfg=cfg: O.ashape_row_ranges(i, cfg.sink, cfg.window)
+            elif r.kind == O.BSPARSE:
+                fns[h] = lambda i, r=r: O.bs_row_ranges(i, r.J)
+            else:
+                cover = O.slash_offset_set(r.offs, n, 64)
+                runs = O.span_runs(cover, 64)
+                fns[h] = lambda i, r=r, cover=cover, runs=runs: O.vs_row_ranges(i, r.cols, cover, 64, runs)
+    else:
+        v64 = O.widen(p.V[0, kv], p.dtype)
+
+    def job(j):
+        if j[0] == "index":
+            return j, _check_index(p, given, cnt, j[1], k64)
+        if j[0] == "edges":
+            return j, res[j[1]].edges
+        h, part = j[1], j[2]
+        rr = rows[part::parts]
+        if sampled:
+            o, _ = O.attend_rows_ranges(_f32(p.Q[0, h][rr], p.dtype), k32, v32, rr, fns[h], sc)
+        else:
+            # every row: dense products of row chunks against the keys up to
+            # the chunk's last row, masked
+            o, _ = O.attend_rows(_Widened(_f32(p.Q[0, h], p.dtype)), k64, v64, rr, res[h].mask_fn, sc)
+        return j, o
+
+    jobs = ([("attn", h, part) for h in hs for part in range(parts)] + [("index", h) for h in hs] +
+            [("edges", h) for h in hs])
+    ndiff = 0
+    with threadpool_limits(limits=1), ThreadPoolExecutor(nt) as ex:
+        for j, r in ex.map(job, jobs):
+            if j[0] == "attn":
+                ref[j[1], j[2]::parts] = r
+            elif j[0] == "index":
+                ndiff += r
+            else:
+                assert int(ke[0, j[1]]) == r, f"kept edges of head {j[1]}: {ke[0, j[1]]} vs {r}"
+    return ndiff
+
+
+@pytest.mark.timeout(700)
 @pytest.mark.parametrize("w", [2, 3, 4, 5])
 def test_full_size_layer(w):
     import torch
     t0 = time.time()
     p = gen.make_workload(w)
     U.log(f"workload {p.name}: generated in {time.time() - t0:.0f}s")
-    n, nq = p.n, (p.n + 63) // 64
+    n = p.n
     g = p.Hq // p.Hkv
     sc = p.eff_scale
     prob = M.make_problem(p.B, p.Hq, p.Hkv, p.n, p.dh, p.dtype, "f32", p.scale)
@@ -102,72 +188,35 @@ def test_full_size_layer(w):
     assert int(t["status"].item()) == 0
     U.log(f"  GPU layer done ({time.time() - t0:.0f}s)")
     if p.rows is None:
-        rows_all = np.arange(n, dtype=np.int64)
+        rows = np.arange(n, dtype=np.int64)
     else:
-        rows_all = np.unique(np.concatenate([p.rows, p.edge_rows])).astype(np.int64)
-    vi = buf["vert_idx"].cpu().numpy()
-    si = buf["slash_idx"].cpu().numpy()
+        rows = np.unique(np.concatenate([p.rows, p.edge_rows])).astype(np.int64)
+    given = U.gpu_given(p, buf)
+    cnt = buf["blk_cnt"].cpu().numpy()
     ke = t["kept_edges"].cpu().numpy()
-    del Q, K, V
+    og = Og[0][:, torch.from_numpy(rows).cuda()].cpu().numpy()          # [Hq, R, dh]
+    del Q, K, V, Og, buf, t
+    torch.cuda.empty_cache()
+    nt = _threads()
 
-    for num, h in enumerate(_checked_heads(p)):
-        cfg = p.heads[h]
-        b = 0
-        kv = h // g
-        what = f"{p.name} head {h} ({gen.KIND_NAMES[cfg.kind]})"
-        q = _f32(p.Q[b, h], p.dtype)
-        k = _f32(p.K[b, kv], p.dtype)
-        v = _f32(p.V[b, kv], p.dtype)
-        # ---- index against the oracle's
-        if cfg.kind == gen.VSLASH:
-            c, r = O.vs_proxy_scores(q.astype(np.float64), k.astype(np.float64), cfg.last_q, sc)
-            cols, offs = vi[b, h][vi[b, h] >= 0], si[b, h][si[b, h] >= 0]
-            d1, e1 = U.check_selection(cols, c, cfg.n_vertical, f"{what} columns")
-            d2, e2 = U.check_selection(offs, r, cfg.n_slash, f"{what} offsets")
-            U.log(f"  {what}: index matches ({d1 + d2} near-tie differences)")
-            cover = O.slash_offset_set(offs, n, 64)
-            assert int(ke[b, h]) == O.vs_edges(n, cols, offs, 64)
-            xs = np.nonzero(cover)[0] - 63
-            colset = np.asarray(cols, dtype=np.int64)
-
-            def keys_fn(i, xs=xs, colset=colset):
-                j = 64 * (i // 64) - xs
-                j = j[(j >= 0) & (j <= i)]
-                return np.union1d(j, colset[colset <= i])
-            mask_fn = lambda rr, nk: O.vs_mask(rr, nk, n, cols, offs, 64, cover)
-        elif cfg.kind == gen.BSPARSE:
-            bi = buf["blk_idx"][b, h].cpu().numpy()
-            bc = buf["blk_cnt"][b, h].cpu().numpy()
-            J = [bi[u, :bc[u]].astype(np.int64) for u in range(nq)]
-            scores = O.bs_block_scores(q.astype(np.float64), k.astype(np.float64), sc)
-            nd = 0
-            for u in range(nq):
-                row = scores[u, :u + 1].copy()
-                if cfg.force_flags & gen.FORCE_FIRST_BLOCK:
-                    row[0] = np.inf
-                if cfg.force_flags & gen.FORCE_DIAG_BLOCK:
-                    row[u] = np.inf
-                d, _ = U.check_selection(J[u], row, cfg.topk_blocks, f"{what} block {u}")
-                nd += d
-            U.log(f"  {what}: index matches ({nd} near-tie differences)")
-            del scores
-            assert int(ke[b, h]) == O.bs_edges(n, J)
-            keys_fn = lambda i, J=J: O.bs_row_keys(i, J)
-            mask_fn = lambda rr, nk: O.bs_mask(rr, nk, J)
-        else:
-            assert int(ke[b, h]) == int(O.ashape_row_counts(n, cfg.sink, cfg.window).sum())
-            keys_fn = lambda i, cfg=cfg: O.ashape_row_keys(i, cfg.sink, cfg.window)
-            mask_fn = lambda rr, nk, cfg=cfg: O.ashape_mask(rr, nk, cfg.sink, cfg.window)
-        # ---- output rows against the oracle's restricted softmax
-        rows = rows_all if (num == 0 or p.rows is None) else rows_all[:: max(1, len(rows_all) // 512)]
-        og = Og[b, h][torch.from_numpy(rows).cuda()].cpu().numpy()
-        if p.rows is None:
-            ref, _ = O.attend_rows(q.astype(np.float64), k.astype(np.float64), v.astype(np.float64), rows,
-                                   mask_fn, sc)
-        else:
-            ref = _row_refs(q, _Widened(k), _Widened(v), rows, keys_fn, sc, what)
-        U.compare_output(og, ref, p.dtype, f"{what}, {len(rows)} rows")
-        U.log(f"  {what}: done ({time.time() - t0:.0f}s)")
+    # ---- per KV group (its query heads share the widened K and V): every
+    #      head's index against the oracle's estimate, its kept edges and its
+    #      output rows against the oracle's attention on the GPU's index sets
+    ref = np.zeros((p.Hq, len(rows), p.dh))
+    ndiff = 0
+    for kv in range(p.Hkv):
+        hs = list(range(kv * g, (kv + 1) * g))
+        ndiff += _check_group(p, kv, rows, given, cnt, ke, ref, nt)
+        U.log(f"  KV group {kv}: heads {hs[0]}..{hs[-1]} ({', '.join(gen.KIND_NAMES[p.heads[h].kind] for h in hs)}): "
+              f"index, kept edges and oracle rows done ({time.time() - t0:.0f}s)")
+    U.log(f"  index of all {p.Hq} heads matches the oracle's ({ndiff} near-tie differences)")
+    worst = (0.0, 0.0)
+    for h in range(p.Hq):
+        mx, mean = U.compare_output(og[h], ref[h], p.dtype,
+                                    f"{p.name} head {h} ({gen.KIND_NAMES[p.heads[h].kind]}), {len(rows)} rows")
+        worst = (max(worst[0], mx), max(worst[1], mean))
+    U.log(f"  {p.name}: {p.Hq}/{p.Hq} heads x {len(rows)} rows match; worst max-abs {worst[0]:.3e}, "
+          f"worst mean-abs {worst[1]:.3e} ({time.time() - t0:.0f}s)")
 
 
 @pytest.mark.timeout(400)
@@ -224,8 +273,13 @@ def test_full_size_single_launch_vs_index():
     for fn in (M.minf_vs_index_fused, M.minf_vs_index):
         c = torch.zeros((p.B, p.Hq, p.n), dtype=torch.float32, device="cuda")
         r = torch.zeros_like(c)
-        fn(prob, heads, Q, K, buf["vert_idx"], buf["slash_idx"], c, r, buf["ws"])
+        st = torch.zeros(1, dtype=torch.int32, device="cuda")
+        if fn is M.minf_vs_index_fused:
+            fn(prob, heads, Q, K, buf["vert_idx"], buf["slash_idx"], c, r, buf["ws"], status=st)
+        else:
+            fn(prob, heads, Q, K, buf["vert_idx"], buf["slash_idx"], c, r, buf["ws"])
         torch.cuda.synchronize()
+        assert int(st.item()) == 0
         if not scores:
             vi, si = buf["vert_idx"].cpu().numpy(), buf["slash_idx"].cpu().numpy()
         scores.append((c.cpu().numpy(), r.cpu().numpy()))

@@ -5,8 +5,8 @@ minf_sparse_attn; tile lists and kept edges must match exactly and the
 output element by element (bf16 inputs: max-abs 1e-2 and mean-abs 1e-3;
 fp32 inputs: 1e-5).  Level 2: minf_vs_index / minf_bs_index must select the
 oracle's sets except for near-ties (oracle score within 1e-4 relative of the
-k-th threshold).  End to end: when the selections agree, the whole path's
-output matches the oracle's.
+k-th threshold).  End to end: the whole path's output and kept edges match
+the oracle's attention over the GPU's own index sets.
 """
 import numpy as np
 import pytest
@@ -151,11 +151,14 @@ def test_index_and_end_to_end(name):
     M.minf_sparse_attn(prob, heads, Q, K, V, buf["blk_idx"], buf["blk_cnt"], buf["tiles"], O_, None, buf["ws"])
     torch.cuda.synchronize()
     assert int(buf["tiles"]["status"].item()) == 0
-    if exact:
-        U.compare_output(O_.cpu().numpy(), res["O"], p.dtype, f"{name} end-to-end O")
-        ke = buf["tiles"]["kept_edges"].cpu().numpy()
-        for (b, h), hr in res["heads"].items():
-            assert int(ke[b, h]) == hr.edges
+    # the oracle's attention on the GPU's own index sets (the same sets as
+    # the oracle's estimate unless a near-tie differs)
+    U.log(f"  GPU index sets identical to the oracle's: {exact}")
+    ref = O.run_layer(p.Q, p.K, p.V, p.dtype, p.heads, scale=p.scale, given=U.gpu_given(p, buf))
+    U.compare_output(O_.cpu().numpy(), ref["O"], p.dtype, f"{name} end-to-end O")
+    ke = buf["tiles"]["kept_edges"].cpu().numpy()
+    for (b, h), hr in ref["heads"].items():
+        assert int(ke[b, h]) == hr.edges
 
 
 def test_determinism():
