@@ -539,18 +539,24 @@ def main():
     if "vslash" in per_kind and not a.no_vs_single:
         # the Vertical-Slash estimate alone, warm: the two-launch path the layer
         # uses against the single-launch proxy (minf_vs_index_fused)
+        vs_status = torch.zeros(1, dtype=torch.int32, device="cuda")
+
         def vs_ms(fn, reps=20):
-            fn(prob, heads, Q, K, buf["vert_idx"], buf["slash_idx"], None, None, buf["ws"], stream=stream)
+            kw = {"status": vs_status} if fn is M.minf_vs_index_fused else {}
+            fn(prob, heads, Q, K, buf["vert_idx"], buf["slash_idx"], None, None, buf["ws"], stream=stream, **kw)
             ms = []
             for _ in range(reps):
                 e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
                 e0.record(stream)
-                fn(prob, heads, Q, K, buf["vert_idx"], buf["slash_idx"], None, None, buf["ws"], stream=stream)
+                fn(prob, heads, Q, K, buf["vert_idx"], buf["slash_idx"], None, None, buf["ws"], stream=stream, **kw)
                 e1.record(stream)
                 e1.synchronize()
                 ms.append(e0.elapsed_time(e1))
             return sorted(ms)[reps // 2]
         two, one = vs_ms(M.minf_vs_index), vs_ms(M.minf_vs_index_fused)
+        torch.cuda.synchronize()
+        if int(vs_status.item()) != 0:
+            raise RuntimeError("minf_vs_index_fused: a bounded wait ran out (MINF_DEV_WAIT_EXHAUSTED)")
         vs_fused = {"two_launch_ms": round(two, 4), "single_launch_ms": round(one, 4),
                     "what": "Vertical-Slash estimate (proxy, fold, column and slash sums, top-k) alone, warm, "
                             "median of 20: minf_vs_index (the layer's path) vs minf_vs_index_fused"}

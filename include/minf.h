@@ -161,7 +161,8 @@ enum {
   MINF_DEV_BAD_VERTICAL = 1,   /* a column index outside [0, n) or not ascending  */
   MINF_DEV_BAD_SLASH = 2,      /* an offset outside [0, n) or not ascending       */
   MINF_DEV_BAD_BLOCK = 4,      /* a block index outside [0, u] or not ascending   */
-  MINF_DEV_CAPACITY = 8        /* a list outgrew the capacity it was sized with   */
+  MINF_DEV_CAPACITY = 8,       /* a list outgrew the capacity it was sized with   */
+  MINF_DEV_WAIT_EXHAUSTED = 16 /* minf_vs_index_fused: a bounded wait ran out     */
 };
 
 /* Fills *out for the given problem and head table (host only, no GPU work).
@@ -197,15 +198,16 @@ minf_status minf_vs_index(const minf_problem* prob, const minf_head_cfg* heads,
  * sums, so selections can differ only between near-equal scores.  The
  * waits end by construction (a second-pass work-group waits only for work
  * that started before it and waits for nothing); each is still bounded (about
- * a second), and a wait that ran out would leave its key range's column and
- * slash scores NaN rather than unwritten.  The two-launch minf_vs_index is
- * faster on MI355X and remains the path that minf_prefill_ragged and the
- * layer use. */
+ * a second).  A wait that ran out sets MINF_DEV_WAIT_EXHAUSTED in *status
+ * (DEVICE int32, required, OR-ed into; the caller zeroes it first) and
+ * leaves zero column and slash scores for its key range, so the selections
+ * of that call are not to be used.  The two-launch minf_vs_index is faster
+ * on MI355X and remains the path that minf_prefill_ragged and the layer use. */
 minf_status minf_vs_index_fused(const minf_problem* prob, const minf_head_cfg* heads,
                                 const void* Q, const void* K,
                                 int32_t* vert_idx, int32_t* slash_idx,
                                 float* vert_score, float* slash_score,
-                                void* ws, size_t ws_bytes, void* stream);
+                                void* ws, size_t ws_bytes, int32_t* status, void* stream);
 
 /* Block-Sparse index estimation (MInference page, section 2, Eq. 6 and the
  * mean-pooling proxy; blog section 2.3.2).  For every BS head: Q and K are

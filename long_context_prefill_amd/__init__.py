@@ -34,6 +34,7 @@ MINF_F32, MINF_BF16 = 0, 1
 MINF_ASHAPE, MINF_VSLASH, MINF_BSPARSE = 0, 1, 2
 MINF_FORCE_FIRST_BLOCK, MINF_FORCE_DIAG_BLOCK = 1, 2
 MINF_DEV_BAD_VERTICAL, MINF_DEV_BAD_SLASH, MINF_DEV_BAD_BLOCK, MINF_DEV_CAPACITY = 1, 2, 4, 8
+MINF_DEV_WAIT_EXHAUSTED = 16
 
 EXPORTED = ["minf_query_sizes", "minf_vs_index", "minf_vs_index_fused", "minf_bs_index", "minf_build_tiles",
             "minf_sparse_attn", "minf_output_error", "minf_captured_mass", "minf_ragged_ws_bytes",
@@ -88,7 +89,8 @@ def load_library(path: str = LIB_PATH):
     vp = ctypes.c_void_p
     lib.minf_query_sizes.argtypes = [P(MinfProblem), P(MinfHeadCfg), P(MinfSizes)]
     lib.minf_vs_index.argtypes = [P(MinfProblem), P(MinfHeadCfg), vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t, vp]
-    lib.minf_vs_index_fused.argtypes = lib.minf_vs_index.argtypes
+    lib.minf_vs_index_fused.argtypes = [P(MinfProblem), P(MinfHeadCfg), vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t,
+                                        vp, vp]
     lib.minf_bs_index.argtypes = [P(MinfProblem), P(MinfHeadCfg), vp, vp, vp, vp, vp, ctypes.c_size_t, vp]
     lib.minf_build_tiles.argtypes = [P(MinfProblem), P(MinfHeadCfg), vp, vp, vp, vp, P(MinfTiles), vp,
                                      ctypes.c_size_t, vp]
@@ -183,10 +185,11 @@ def minf_vs_index(prob, heads, Q, K, vert_idx, slash_idx, vert_score=None, slash
 
 
 def minf_vs_index_fused(prob, heads, Q, K, vert_idx, slash_idx, vert_score=None, slash_score=None, ws=None,
-                        stream=None):
+                        status=None, stream=None):
     lib = load_library()
     _check(lib.minf_vs_index_fused(ctypes.byref(prob), heads, _ptr(Q), _ptr(K), _ptr(vert_idx), _ptr(slash_idx),
-                                   _ptr(vert_score), _ptr(slash_score), _ptr(ws), _nbytes(ws), _stream(stream)))
+                                   _ptr(vert_score), _ptr(slash_score), _ptr(ws), _nbytes(ws), _ptr(status),
+                                   _stream(stream)))
 
 
 def minf_bs_index(prob, heads, Q, K, blk_idx, blk_cnt, ws=None, stream=None):

@@ -26,6 +26,11 @@ minf_status fail(minf_status s, const char* fmt, ...) {
 
 int64_t round_up(int64_t x, int64_t m) { return (x + m - 1) / m * m; }
 
+// A Block-Sparse row's selection keeps the row's scores in the registers of
+// one work-group (256 threads x 128 scores), so a row holds at most this many
+// key blocks.
+constexpr int64_t kBsMaxBlocks = 256 * 128;
+
 struct Derived {
   int64_t nq = 0, max_v = 0, max_s = 0, max_kb = 0, max_chunks = 0, bm_words = 0, bits_words = 0;
   bool has_a = false, has_vs = false, has_bs = false;
@@ -80,6 +85,9 @@ minf_status validate(const minf_problem* p, const minf_head_cfg* heads, Derived*
         if (c.topk_blocks < 1) return fail(MINF_EINVAL, "head %d: topk_blocks must be >= 1", h);
         if (c.force_flags & ~(MINF_FORCE_FIRST_BLOCK | MINF_FORCE_DIAG_BLOCK))
           return fail(MINF_EINVAL, "head %d: unknown force flags 0x%x", h, c.force_flags);
+        if (d->nq > kBsMaxBlocks)
+          return fail(MINF_EUNSUPPORTED, "head %d: Block-Sparse rows of more than %lld blocks (n > %lld) are not supported",
+                      h, (long long)kBsMaxBlocks, (long long)kBsMaxBlocks * MINF_BLOCK);
         const int64_t k = std::min<int64_t>(c.topk_blocks, d->nq);
         d->ht.a[h] = (int32_t)k;
         d->ht.b[h] = c.force_flags;
@@ -238,14 +246,16 @@ minf_status minf_query_sizes(const minf_problem* prob, const minf_head_cfg* head
 
 static minf_status vs_index_impl(const minf_problem* prob, const minf_head_cfg* heads, const void* Q, const void* K,
                                  int32_t* vert_idx, int32_t* slash_idx, float* vert_score, float* slash_score,
-                                 void* ws, size_t ws_bytes, void* stream, bool fused) {
+                                 void* ws, size_t ws_bytes, int32_t* status, void* stream, bool fused) {
   Derived d;
   minf_status s = validate(prob, heads, &d);
   if (s != MINF_OK) return s;
   if (!d.has_vs) return MINF_OK;
   if (!Q || !K || !vert_idx || !slash_idx) return fail(MINF_EINVAL, "null Q, K or index output");
+  if (fused && !status) return fail(MINF_EINVAL, "minf_vs_index_fused needs a status word");
   if ((s = check_ws(prob, d, ws, ws_bytes)) != MINF_OK) return s;
   minf::VsParams v{};
+  v.status = status;
   v.Q = Q; v.K = K;
   v.vert_idx = vert_idx; v.slash_idx = slash_idx;
   v.vert_score = vert_score; v.slash_score = slash_score;
@@ -264,13 +274,15 @@ static minf_status vs_index_impl(const minf_problem* prob, const minf_head_cfg* 
 minf_status minf_vs_index(const minf_problem* prob, const minf_head_cfg* heads, const void* Q, const void* K,
                           int32_t* vert_idx, int32_t* slash_idx, float* vert_score, float* slash_score,
                           void* ws, size_t ws_bytes, void* stream) {
-  return vs_index_impl(prob, heads, Q, K, vert_idx, slash_idx, vert_score, slash_score, ws, ws_bytes, stream, false);
+  return vs_index_impl(prob, heads, Q, K, vert_idx, slash_idx, vert_score, slash_score, ws, ws_bytes, nullptr, stream,
+                       false);
 }
 
 minf_status minf_vs_index_fused(const minf_problem* prob, const minf_head_cfg* heads, const void* Q, const void* K,
                                 int32_t* vert_idx, int32_t* slash_idx, float* vert_score, float* slash_score,
-                                void* ws, size_t ws_bytes, void* stream) {
-  return vs_index_impl(prob, heads, Q, K, vert_idx, slash_idx, vert_score, slash_score, ws, ws_bytes, stream, true);
+                                void* ws, size_t ws_bytes, int32_t* status, void* stream) {
+  return vs_index_impl(prob, heads, Q, K, vert_idx, slash_idx, vert_score, slash_score, ws, ws_bytes, status, stream,
+                       true);
 }
 
 minf_status minf_bs_index(const minf_problem* prob, const minf_head_cfg* heads, const void* Q, const void* K,

@@ -124,6 +124,7 @@ struct VsParams {
   HeadTable ht;     // VSLASH: a = last_q, b = #columns, c = #offsets
   VsWs ws;
   char* ws_base;
+  int32_t* status;  // minf_vs_index_fused: MINF_DEV_WAIT_EXHAUSTED when a bounded wait runs out
 };
 hipError_t launch_vs_index(const VsParams& p, hipStream_t st);
 hipError_t launch_vs_index_fused(const VsParams& p, hipStream_t st);   // the proxy in one launch

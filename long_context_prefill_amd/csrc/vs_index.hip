@@ -656,23 +656,17 @@ __global__ __launch_bounds__(256) void vs_fused_kernel(VsParams P, VsFusedMeta M
     }
     __syncthreads();
     if (!s_val) {
-      // the wait ran out (the work order rules this out): mark this range's
-      // column sums and home-offset slash sums as NaN instead of leaving them
-      // unwritten
-      // (the quiet-NaN bit pattern is stored as an integer: this file is
-      // compiled without NaN semantics)
-      constexpr int32_t kQNaN = 0x7fc00000;
-      int32_t* cdst = reinterpret_cast<int32_t*>(P.vert_score ? P.vert_score
-                                                              : reinterpret_cast<float*>(P.ws_base + P.ws.cbuf)) +
-                      (size_t)bh * P.n;
-      int32_t* rdst = reinterpret_cast<int32_t*>(P.slash_score ? P.slash_score
-                                                               : reinterpret_cast<float*>(P.ws_base + P.ws.rbuf)) +
-                      (size_t)bh * P.n;
+      // the wait ran out (the work order rules this out): report it in the
+      // caller's status word and leave defined (zero) column and slash sums
+      // for this range rather than unwritten ones
+      float* cdst = (P.vert_score ? P.vert_score : reinterpret_cast<float*>(P.ws_base + P.ws.cbuf)) + (size_t)bh * P.n;
+      float* rdst = (P.slash_score ? P.slash_score : reinterpret_cast<float*>(P.ws_base + P.ws.rbuf)) + (size_t)bh * P.n;
       const int j0 = range * kVsGroupKeys, j1 = min(j0 + kVsGroupKeys, P.n);
       for (int j = j0 + (int)threadIdx.x; j < j1; j += 256) {
-        cdst[j] = kQNaN;
-        rdst[P.n - 1 - j] = kQNaN;     // offset d is home to the range holding key n - 1 - d
+        cdst[j] = 0.f;
+        rdst[P.n - 1 - j] = 0.f;     // offset d is home to the range holding key n - 1 - d
       }
+      if (threadIdx.x == 0) atomicOr(P.status, (int)MINF_DEV_WAIT_EXHAUSTED);
       return;
     }
     fused_task<T, DH, 2>(P, bh, range, ptile[wave], red, dacc[wave]);

@@ -87,6 +87,8 @@ def test_query_sizes_exact_slash_pairs(lib):
     (dict(), [gen.bsparse(0)] + HEADS[1:], M.MINF_EINVAL),
     (dict(), [gen.bsparse(2, 8)] + HEADS[1:], M.MINF_EINVAL),
     (dict(), [gen.HeadCfg(7)] + HEADS[1:], M.MINF_EINVAL),
+    # a Block-Sparse row of more than 32768 key blocks (n > 2^21) is refused
+    (dict(n=(1 << 21) + 1, Hq=4, Hkv=1), HEADS, M.MINF_EUNSUPPORTED),
 ])
 def test_validation_errors(lib, kw, heads, status):
     p = _prob(**kw)
@@ -109,6 +111,9 @@ def test_calls_reject_before_launch(lib):
     assert st == M.MINF_EWORKSPACE
     st = lib.minf_bs_index(ctypes.byref(p), h, fake, fake, None, fake, fake, 1 << 40, None)
     assert st == M.MINF_EINVAL
+    # the single-launch proxy needs its status word
+    st = lib.minf_vs_index_fused(ctypes.byref(p), h, fake, fake, fake, fake, None, None, fake, 1 << 40, None, None)
+    assert st == M.MINF_EINVAL and "status" in lib.minf_last_error().decode()
     st = lib.minf_build_tiles(ctypes.byref(p), h, fake, fake, fake, fake, ctypes.byref(ts), fake, 1 << 40, None)
     assert st == M.MINF_EINVAL          # tiles has no kept_edges / status
     st = lib.minf_sparse_attn(ctypes.byref(p), h, fake, fake, None, fake, fake, ctypes.byref(ts), fake, None,

@@ -37,10 +37,14 @@ def _run(p, fused, fill=None):
     Q, K, V = U.device_inputs(p)
     c = torch.zeros((p.B, p.Hq, p.n), dtype=torch.float32, device="cuda")
     r = torch.zeros_like(c)
-    vs = M.minf_vs_index_fused if fused else M.minf_vs_index
-    vs(prob, heads, Q, K, buf["vert_idx"], buf["slash_idx"], c, r, buf["ws"])
+    st = torch.zeros(1, dtype=torch.int32, device="cuda")
+    if fused:
+        M.minf_vs_index_fused(prob, heads, Q, K, buf["vert_idx"], buf["slash_idx"], c, r, buf["ws"], status=st)
+    else:
+        M.minf_vs_index(prob, heads, Q, K, buf["vert_idx"], buf["slash_idx"], c, r, buf["ws"])
     M.minf_bs_index(prob, heads, Q, K, buf["blk_idx"], buf["blk_cnt"], buf["ws"])
     torch.cuda.synchronize()
+    assert int(st.item()) == 0, "a bounded wait of the single-launch proxy ran out"
     return buf, c.cpu().numpy(), r.cpu().numpy()
 
 
