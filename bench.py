@@ -121,6 +121,40 @@ def copy_probe(mib, reps):
     print(json.dumps({"copy_bytes": mib << 20, "reps": reps}), flush=True)
 
 
+def measured_peaks():
+    """The box's own ceilings, measured beside the vendor figures: a bf16
+    matrix product (torch.mm, 8192^3, hipBLASLt) and a device-to-device copy
+    of 2 GiB (read + write bytes), medians of 10 event-timed runs each."""
+    import torch
+    n = 8192
+    a = torch.randn(n, n, device="cuda").to(torch.bfloat16)
+    b = torch.randn(n, n, device="cuda").to(torch.bfloat16).contiguous()
+    x = torch.ones(1 << 29, dtype=torch.float32, device="cuda")
+    y = torch.empty_like(x)
+
+    def med(fn, reps=10):
+        for _ in range(3):
+            fn()
+        ms = []
+        for _ in range(reps):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            fn()
+            e1.record()
+            e1.synchronize()
+            ms.append(e0.elapsed_time(e1))
+        return sorted(ms)[reps // 2]
+    t_mm = med(lambda: torch.mm(a, b))
+    t_cp = med(lambda: y.copy_(x))
+    out = {"bf16_gemm_tflops": round(2.0 * n ** 3 / (t_mm * 1e-3) / 1e12, 1),
+           "copy_gbs": round(2.0 * x.numel() * 4 / (t_cp * 1e-3) / 1e9, 1),
+           "what": "torch.mm bf16 8192x8192x8192 and a 2 GiB device copy (bytes read + written), "
+                   "median of 10 event-timed runs each"}
+    del a, b, x, y
+    torch.cuda.empty_cache()
+    return out
+
+
 def cpu_baseline(p, workers):
     """The oracle as it stands, timed on a bounded sample of the same layer:
     full index estimation of half of the heads (kinds in the layer's
@@ -137,7 +171,7 @@ def cpu_baseline(p, workers):
     sample = []
     for k, hs in kinds.items():
         sample += hs[:max(1, len(hs) // 2)]
-    R = 4096
+    R = min(4096, p.n)
     rng = np.random.default_rng(0)
     rows = np.sort(rng.choice(p.n, R, replace=False))
     sc = p.eff_scale
@@ -402,6 +436,8 @@ def main():
     ap.add_argument("--search-eps", type=float, default=0.05, help="error bound of the pattern search")
     ap.add_argument("--ragged", action="store_true",
                     help="only time a ragged batch of 8 requests against the same batch padded to its longest")
+    ap.add_argument("--no-peaks", action="store_true", help="skip measuring the box's bf16 GEMM and copy ceilings")
+    ap.add_argument("--peaks", action="store_true", help="only measure the box's bf16 GEMM and copy ceilings")
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="only run a plain device copy of this many MiB (memory-counter calibration)")
     a = ap.parse_args()
@@ -412,6 +448,9 @@ def main():
 
     if a.copy_mib:
         copy_probe(a.copy_mib, max(1, a.steps))
+        return
+    if a.peaks:
+        print(json.dumps(measured_peaks()), flush=True)
         return
     if a.crossover:
         crossover(a)
@@ -577,6 +616,14 @@ def main():
                                     "ragged_kept_edge_tflops")}
         log(f"ragged batch in {time.time() - t0:.1f}s")
 
+    peaks = None
+    if not a.no_peaks:
+        t0 = time.time()
+        peaks = measured_peaks()
+        peaks["attn_frac_of_measured_gemm"] = round(kern_tflops / peaks["bf16_gemm_tflops"], 4)
+        peaks["index_frac_of_measured_copy"] = round(idx_gbs / peaks["copy_gbs"], 4)
+        log(f"measured peaks in {time.time() - t0:.1f}s")
+
     cpu = None
     if not a.no_cpu_baseline:
         try:
@@ -627,6 +674,7 @@ def main():
                      "kernel": ATTN_KERNEL if (p.dtype == "bf16" and p.dh == 128) else "attn_kernel",
                      "per_launch_flops": flops, "avg_launch_ms": round(ms_kernel, 4),
                      "launches_timed": len(kern)},
+        "measured_peaks": peaks,
         "dense_baseline": dense_bl,
         "exact_slash_pairs": exact,
         "vs_single_launch": vs_fused,

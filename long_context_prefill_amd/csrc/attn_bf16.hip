@@ -500,7 +500,34 @@ __device__ __forceinline__ void attn_item(const AttnParams& P, const int b, cons
     }
     return d;
   };
-  auto describe = [&](int k) { return decode(k, fetch(k)); };
+  // Plain chunks (32 keys inside [0, n), every pair of this wave's rows
+  // kept: one affine copy, no per-element test) are recognised with a few
+  // scalar comparisons; every other chunk takes the general decode above.
+  // * A-shape window chunk at kstart: plain iff plo <= kstart <= phi, i.e.
+  //   kstart >= rlast - w + 1 (inside every row's window), kstart + 31 <=
+  //   rw0 (causal for the first row), kstart + 31 <= whi and <= n - 1.
+  // * Block-Sparse: a selected block below the diagonal (0 <= vb < u).
+  // * Vertical-Slash span chunk [lo, hi] of offsets: plain iff it is 32
+  //   wide, kstart = 64u - hi >= 0, kstart + 31 <= min(rw0, n - 1), i.e.
+  //   hi >= 31 - 32 * wave, and pairs are not tested one by one (exact).
+  const int wbase = wlo - 32 * Ca;
+  const int plo = max(rlast - win + 1, 0);
+  const int phi = min(min(rw0, whi) - 31, n - 32);
+  const int hmin = 31 - 32 * wave;
+  auto decode_fast = [&](int k, const Raw& r) {
+    if constexpr (KIND == MINF_ASHAPE) {
+      const int ks = wbase + 32 * k;
+      if (k >= Ca && ks >= plo && ks <= phi) return Chunk{ks, 0, 0, kFast};
+    } else if constexpr (KIND == MINF_BSPARSE) {
+      if (r.a >= 0 && r.a < u) return Chunk{64 * r.a + 32 * (k & 1), 0, 0, kFast};
+    } else {
+      const int ks = row0 - r.b;
+      if (k < Ca && !exact && r.b - r.a == 31 && ks >= 0 && r.b >= hmin && ks <= n - 32)
+        return Chunk{ks, 0, 0, kFast};
+    }
+    return decode(k, r);
+  };
+  auto describe = [&](int k) { return decode_fast(k, fetch(k)); };
 
   // ---- copy offsets.  Wave w copies rows 16w + 4i + lane/16 (i = 0..3) of
   //      each tile; lane l writes LDS piece l%16 of its row, which holds the
@@ -587,11 +614,11 @@ __device__ __forceinline__ void attn_item(const AttnParams& P, const int b, cons
   };
   // exclusion (section 5.1): pairs outside the candidate set are -inf before
   // the maximum
+  // A chunk without any kept pair for this wave (kNone) takes the same
+  // in-place path with every keep-bit clear (keep_bits gives 0 for it), so
+  // the scores are only ever rewritten where they stand.
   auto apply_mask = [&](floatx16& s, const Chunk& d, uint32_t bits) {
-    if (d.flags & kNone) {
-      #pragma unroll
-      for (int i = 0; i < 16; ++i) s[i] = kNegInf;
-    } else if (d.flags & kMask) {
+    if (d.flags & (kMask | kNone)) {
       // (the vector is reinterpreted whole: bit-casting single elements of a
       // vector has been miscompiled into reads of element 0)
       u32x16 v = __builtin_bit_cast(u32x16, s);
@@ -701,17 +728,19 @@ __device__ __forceinline__ void attn_item(const AttnParams& P, const int b, cons
   if (kPrefetch && C > 2) rn = fetch(next_of(kc));
   wait_copies_and_barrier();
   uint32_t bits0 = keep_bits(d0);
-  floatx16 s_cur;
+  // the scores of chunk j live in sA for even j and in sB for odd j: each
+  // iteration reads one and writes the other, so no copy between them
+  floatx16 sA, sB;
   {
     u32x4 kop[8];
     read_k(0, kop);
-    s_cur = qk(kop);
+    sA = qk(kop);
   }
   // iteration 0 rewrites the K half of slot 0, which both waves just read
   wait_copies_and_barrier();
 
   // STEADY: chunks j+1 .. j+3 exist (j+1 .. j+2 for A-shape; no bound tests)
-  auto iteration = [&](const int j, const int sl, auto steady) {
+  auto iteration = [&](const int j, const int sl, auto steady, floatx16& s_cur, floatx16& s_nxt) {
     constexpr bool STEADY = decltype(steady)::value;
     // slot sl holds K and V of chunk j, slot sl^1 holds K of chunk j+1.
     // Kinds with list entries decode chunk j+2 from the entries fetched
@@ -724,7 +753,7 @@ __device__ __forceinline__ void attn_item(const AttnParams& P, const int b, cons
     if constexpr (kPrefetch) {
       if (more2) {
         advance();
-        d2 = decode(kc, rn);
+        d2 = decode_fast(kc, rn);
         if (STEADY || j + 3 < C) rn = fetch(next_of(kc));
       }
     }
@@ -765,7 +794,7 @@ __device__ __forceinline__ void attn_item(const AttnParams& P, const int b, cons
     // of one keep the matrix unit busy while the other runs its scalar and
     // copy work: measured 4% faster at 128K)
     __builtin_amdgcn_s_setprio(1);
-    const floatx16 s_next = qk(kop);
+    s_nxt = qk(kop);
     read_v(sl, vop);
     u32x4 pb[2];
     #pragma unroll
@@ -794,7 +823,6 @@ __device__ __forceinline__ void attn_item(const AttnParams& P, const int b, cons
       #pragma unroll
       for (int mb = 0; mb < 4; ++mb) acc[mb] = mma32(vop[st][mb], pb[st], acc[mb]);
     __builtin_amdgcn_s_setprio(0);
-    s_cur = s_next;
     d0 = d1;
     d1 = d2;
     bits0 = bits1;
@@ -802,16 +830,16 @@ __device__ __forceinline__ void attn_item(const AttnParams& P, const int b, cons
 
   int j = 0;
   for (; j + (kPrefetch ? 4 : 3) < C; j += 2) {
-    iteration(j, 0, std::true_type{});
+    iteration(j, 0, std::true_type{}, sA, sB);
     wait_copies_and_barrier();
-    iteration(j + 1, 1, std::true_type{});
+    iteration(j + 1, 1, std::true_type{}, sB, sA);
     wait_copies_and_barrier();
   }
   for (; j < C; j += 2) {
-    iteration(j, 0, std::false_type{});
+    iteration(j, 0, std::false_type{}, sA, sB);
     if (j + 1 >= C) break;
     wait_copies_and_barrier();
-    iteration(j + 1, 1, std::false_type{});
+    iteration(j + 1, 1, std::false_type{}, sB, sA);
     if (j + 2 >= C) break;
     wait_copies_and_barrier();
   }
