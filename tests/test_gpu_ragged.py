@@ -7,7 +7,10 @@ slash or block crossing a sample boundary.
   alone through the four calls (minf_vs_index, minf_bs_index,
   minf_build_tiles, minf_sparse_attn), kept edges included;
 * changing one sample's data leaves every other sample's output unchanged;
-* A-shape heads (no index estimation) match the oracle per sample.
+* A-shape heads (no index estimation) match the oracle per sample;
+* every pattern kind of every sample matches the oracle run on the sample's
+  GPU index sets, whose selections match the oracle's estimate except
+  near-ties.
 """
 import numpy as np
 import pytest
@@ -128,3 +131,51 @@ def test_ragged_ashape_matches_oracle():
         U.compare_output(out[b][None], ref["O"], s.dtype, f"ragged sample {b}")
         for h, cfg in enumerate(heads):
             assert kept[b, h] == O.ashape_row_counts(s.n, cfg.sink, cfg.window).sum()
+
+
+@pytest.mark.parametrize("name", list(RAGGED))
+def test_ragged_matches_oracle_all_kinds(name):
+    """Every pattern kind of every packed sample against the oracle.  A
+    packed sample's index sets stay inside the workspace, so they are taken
+    from the same sample run alone, which the packed run equals bit for bit
+    (checked here again): those selections must match the oracle's estimate
+    except near-ties, and the packed output rows and kept edges must match
+    the oracle's attention over them."""
+    c = RAGGED[name]
+    base = [gen.vslash(64, 40, 60), gen.bsparse(4), gen.ashape(16, 100), gen.vslash(32, 10, 30),
+            gen.bsparse(3, gen.FORCE_FIRST_BLOCK | gen.FORCE_DIAG_BLOCK), gen.ashape(0, 200), gen.vslash(64, 200, 8),
+            gen.bsparse(100)]
+    heads = [base[h % len(base)] for h in range(c["Hq"])]
+    samples = _samples(c["lens"], c["Hq"], c["Hkv"], c["dh"], c["dtype"], heads, seed=140)
+    out, ls, kept = _run_ragged(samples, heads, max(c["lens"]), c["dtype"])
+    import torch
+    for b, s in enumerate(samples):
+        prob = U.make_prob(s, "f32")
+        hh = M.make_heads(s.heads)
+        buf = M.alloc_buffers(prob, hh)
+        Q, K, V = U.device_inputs(s)
+        O1 = torch.zeros((1, s.Hq, s.n, s.dh), dtype=torch.float32, device="cuda")
+        M.run_layer(prob, hh, Q, K, V, O1, buf=buf)
+        torch.cuda.synchronize()
+        assert np.array_equal(out[b], O1[0].cpu().numpy()), (name, b)
+        est = O.run_layer(s.Q, s.K, s.V, s.dtype, s.heads, scale=s.scale, attend=False)
+        given = U.gpu_given(s, buf)
+        for (bb, h), r in est["heads"].items():
+            cfg = s.heads[h]
+            if r.kind == O.VSLASH:
+                cols, offs = given[(bb, h)]
+                U.check_selection(cols, r.c, cfg.n_vertical, f"sample {b} head {h} columns")
+                U.check_selection(offs, r.r, cfg.n_slash, f"sample {b} head {h} offsets")
+            elif r.kind == O.BSPARSE:
+                sc = O.bs_block_scores(O.widen(s.Q[0, h], s.dtype),
+                                       O.widen(s.K[0, O.kv_head(h, s.Hq, s.Hkv)], s.dtype), s.eff_scale)
+                J = given[(bb, h)]
+                Jm = np.full((len(J), max(1, max(len(x) for x in J))), -1, dtype=np.int64)
+                for u, x in enumerate(J):
+                    Jm[u, :len(x)] = x
+                U.check_block_selections(Jm, [len(x) for x in J], sc, cfg.topk_blocks, cfg.force_flags,
+                                         f"sample {b} head {h}")
+        ref = O.run_layer(s.Q, s.K, s.V, s.dtype, s.heads, scale=s.scale, given=given)
+        U.compare_output(out[b][None], ref["O"], s.dtype, f"{name} packed sample {b} (n={s.n})")
+        for h in range(s.Hq):
+            assert kept[b, h] == ref["heads"][(0, h)].edges, (name, b, h)
