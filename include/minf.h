@@ -252,6 +252,26 @@ minf_status minf_sparse_attn(const minf_problem* prob, const minf_head_cfg* head
                              void* O, float* lse,
                              void* ws, size_t ws_bytes, void* stream);
 
+/* minf_sparse_attn without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation).  Same arguments, results and errors as
+ * minf_sparse_attn, minus ws / ws_bytes: the attention scheduler's scratch
+ * (unit costs and order, XCD assignment, the item queue and its counters)
+ * lives in a file-scope device array of the library, 8 MiB per device, held
+ * until the process ends.  A problem whose scheduler needs more (about 2M
+ * (batch, head, query block) items, e.g. B * Hq * ceil(n / 64) > 2 million)
+ * is refused with MINF_EWORKSPACE before anything is queued.  The call
+ * allocates nothing; it looks up the array's address on the current device
+ * the first time it runs there (the stream must belong to the current
+ * device).  Every call on one device shares that device's array, and the
+ * scheduler rewrites all of it on each call (nothing needs clearing between
+ * calls), so calls that overlap in time on one device -- on different
+ * streams or from several threads -- race: order them on one stream. */
+minf_status minf_sparse_attn_static(const minf_problem* prob, const minf_head_cfg* heads,
+                                    const void* Q, const void* K, const void* V,
+                                    const int32_t* blk_idx, const int32_t* blk_cnt,
+                                    const minf_tiles* tiles, void* O, float* lse, void* stream);
+
 /* Per-head output error, for the offline kernel-aware pattern search
  * (MInference page sections 3.1 and 6.3; blog section 2.3.1, Eq. 2: each
  * candidate pattern's attention is compared with dense attention on a

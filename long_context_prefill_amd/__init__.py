@@ -13,6 +13,7 @@ Entry points (same names and argument order as include/minf.h):
     minf_bs_index(prob, heads, Q, K, blk_idx, blk_cnt, ws, stream=None)
     minf_build_tiles(prob, heads, vert_idx, slash_idx, blk_idx, blk_cnt, tiles, ws, stream=None)
     minf_sparse_attn(prob, heads, Q, K, V, blk_idx, blk_cnt, tiles, O, lse, ws, stream=None)
+    minf_sparse_attn_static(...)  the same without a workspace (static scratch)
     minf_output_error(prob, O, O_ref, err, stream=None)
     minf_captured_mass(prob, lse, lse_ref, mass, stream=None)
     minf_ragged_ws_bytes(prob, heads) -> int
@@ -37,7 +38,7 @@ MINF_DEV_BAD_VERTICAL, MINF_DEV_BAD_SLASH, MINF_DEV_BAD_BLOCK, MINF_DEV_CAPACITY
 MINF_DEV_WAIT_EXHAUSTED = 16
 
 EXPORTED = ["minf_query_sizes", "minf_vs_index", "minf_vs_index_fused", "minf_bs_index", "minf_build_tiles",
-            "minf_sparse_attn", "minf_output_error", "minf_captured_mass", "minf_ragged_ws_bytes",
+            "minf_sparse_attn", "minf_sparse_attn_static", "minf_output_error", "minf_captured_mass", "minf_ragged_ws_bytes",
             "minf_prefill_ragged", "minf_timing_start",
             "minf_timing_read", "minf_status_string", "minf_last_error", "minf_version"]
 
@@ -96,13 +97,15 @@ def load_library(path: str = LIB_PATH):
                                      ctypes.c_size_t, vp]
     lib.minf_sparse_attn.argtypes = [P(MinfProblem), P(MinfHeadCfg), vp, vp, vp, vp, vp, P(MinfTiles), vp, vp,
                                      vp, ctypes.c_size_t, vp]
+    lib.minf_sparse_attn_static.argtypes = [P(MinfProblem), P(MinfHeadCfg), vp, vp, vp, vp, vp, P(MinfTiles), vp,
+                                            vp, vp]
     lib.minf_output_error.argtypes = [P(MinfProblem), vp, vp, vp, vp]
     lib.minf_captured_mass.argtypes = [P(MinfProblem), vp, vp, vp, vp]
     lib.minf_ragged_ws_bytes.argtypes = [P(MinfProblem), P(MinfHeadCfg), P(ctypes.c_int64)]
     lib.minf_prefill_ragged.argtypes = [P(MinfProblem), P(MinfHeadCfg), P(ctypes.c_int32), vp, vp, vp, vp, vp, vp, vp,
                                         vp, ctypes.c_size_t, vp]
     for f in ("minf_query_sizes", "minf_vs_index", "minf_vs_index_fused", "minf_bs_index", "minf_build_tiles",
-              "minf_sparse_attn",
+              "minf_sparse_attn", "minf_sparse_attn_static",
               "minf_output_error", "minf_captured_mass", "minf_ragged_ws_bytes", "minf_prefill_ragged"):
         getattr(lib, f).restype = ctypes.c_int
     lib.minf_timing_start.argtypes = [ctypes.c_int32]
@@ -212,6 +215,14 @@ def minf_sparse_attn(prob, heads, Q, K, V, blk_idx, blk_cnt, tiles: Optional[dic
     _check(lib.minf_sparse_attn(ctypes.byref(prob), heads, _ptr(Q), _ptr(K), _ptr(V), _ptr(blk_idx),
                                 _ptr(blk_cnt), ctypes.byref(ts), _ptr(O), _ptr(lse), _ptr(ws), _nbytes(ws),
                                 _stream(stream)))
+
+
+def minf_sparse_attn_static(prob, heads, Q, K, V, blk_idx, blk_cnt, tiles: Optional[dict], O, lse=None,
+                            stream=None):
+    lib = load_library()
+    ts = tiles_struct(tiles or {})
+    _check(lib.minf_sparse_attn_static(ctypes.byref(prob), heads, _ptr(Q), _ptr(K), _ptr(V), _ptr(blk_idx),
+                                       _ptr(blk_cnt), ctypes.byref(ts), _ptr(O), _ptr(lse), _stream(stream)))
 
 
 def minf_output_error(prob, O, O_ref, err, stream=None):

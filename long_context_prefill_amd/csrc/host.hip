@@ -7,6 +7,7 @@
 #include <string.h>
 
 #include <algorithm>
+#include <mutex>
 #include <vector>
 
 #include "common.h"
@@ -185,6 +186,35 @@ minf_status hip_status(hipError_t e, const char* what) {
   return fail(MINF_EHIP, "%s: %s", what, hipGetErrorString(e));
 }
 
+// Scratch of minf_sparse_attn_static (the attention scheduler's unit costs,
+// order, XCD assignment, item queue and queue counters), a file-scope device
+// array: each device the library runs on holds its own copy until the
+// process ends.  Host code never passes the array's name to a kernel (on the
+// host it stands for no device address): the address comes from
+// hipGetSymbolAddress, once per device, with that device current.
+constexpr size_t kScratchBytes = size_t(8) << 20;
+constexpr int kMaxDevices = 64;
+__device__ __align__(256) char scratch[kScratchBytes];
+std::mutex g_scratch_mu;
+char* g_scratch_ptr[kMaxDevices] = {};
+
+minf_status scratch_on_current_device(char** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(MINF_EHIP, "minf_sparse_attn_static: hipGetDevice: %s", hipGetErrorString(e));
+  if (dev < 0 || dev >= kMaxDevices) return fail(MINF_EUNSUPPORTED, "minf_sparse_attn_static: device %d", dev);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p)
+      return fail(MINF_EHIP, "minf_sparse_attn_static: hipGetSymbolAddress: %s", hipGetErrorString(e));
+    g_scratch_ptr[dev] = static_cast<char*>(p);
+  }
+  *out = g_scratch_ptr[dev];
+  return MINF_OK;
+}
+
 // Event pairs of minf_timing_start() / minf_timing_read(): pair i brackets
 // the main attention kernel of the i-th minf_sparse_attn call since the start.
 struct Timing {
@@ -339,22 +369,27 @@ minf_status minf_build_tiles(const minf_problem* prob, const minf_head_cfg* head
                     "minf_build_tiles launch");
 }
 
-minf_status minf_sparse_attn(const minf_problem* prob, const minf_head_cfg* heads, const void* Q, const void* K,
-                             const void* V, const int32_t* blk_idx, const int32_t* blk_cnt, const minf_tiles* tiles,
-                             void* O, float* lse, void* ws, size_t ws_bytes, void* stream) {
-  Derived d;
-  minf_status s = validate(prob, heads, &d);
+// Checks shared by minf_sparse_attn and minf_sparse_attn_static.
+static minf_status attn_checks(const minf_problem* prob, const minf_head_cfg* heads, const void* Q, const void* K,
+                               const void* V, const int32_t* blk_idx, const int32_t* blk_cnt, const minf_tiles* tiles,
+                               void* O, Derived* d) {
+  minf_status s = validate(prob, heads, d);
   if (s != MINF_OK) return s;
   if (!Q || !K || !V || !O) return fail(MINF_EINVAL, "null Q, K, V or O");
-  if (d.has_bs && (!blk_idx || !blk_cnt)) return fail(MINF_EINVAL, "a Block-Sparse head needs blk_idx and blk_cnt");
-  if (d.has_vs && (!tiles || !tiles->chunk_lo || !tiles->chunk_hi || !tiles->chunk_cnt || !tiles->cols || !tiles->col_cnt))
+  if (d->has_bs && (!blk_idx || !blk_cnt)) return fail(MINF_EINVAL, "a Block-Sparse head needs blk_idx and blk_cnt");
+  if (d->has_vs && (!tiles || !tiles->chunk_lo || !tiles->chunk_hi || !tiles->chunk_cnt || !tiles->cols || !tiles->col_cnt))
     return fail(MINF_EINVAL, "a Vertical-Slash head needs the tile lists from minf_build_tiles");
-  if (d.bits_words > 0 && (!tiles->slash_bits || !tiles->col_bits))
+  if (d->bits_words > 0 && (!tiles->slash_bits || !tiles->col_bits))
     return fail(MINF_EINVAL, "slash_tile=1 with a Vertical-Slash head needs slash_bits and col_bits");
-  if ((s = check_ws(prob, d, ws, ws_bytes)) != MINF_OK) return s;
+  return MINF_OK;
+}
+
+// The attention launch on a workspace `wb` that holds attn_ws(prob, d).total bytes.
+static minf_status attn_launch(const minf_problem* prob, const Derived& d, const void* Q, const void* K, const void* V,
+                               const int32_t* blk_idx, const int32_t* blk_cnt, const minf_tiles* tiles, void* O,
+                               float* lse, char* wb, void* stream, const char* what) {
   const AttnWs w = attn_ws(prob, d);
   minf::AttnParams a{};
-  char* wb = static_cast<char*>(ws);
   a.sched_cost = reinterpret_cast<int64_t*>(wb + w.cost);
   a.sched_order = reinterpret_cast<int32_t*>(wb + w.order);
   a.unit_xcd = reinterpret_cast<int32_t*>(wb + w.uxcd);
@@ -383,7 +418,33 @@ minf_status minf_sparse_attn(const minf_problem* prob, const minf_head_cfg* head
   }
   a.ht = d.ht;
   return hip_status(minf::launch_attn(a, prob->in_dtype == MINF_BF16, prob->dh, static_cast<hipStream_t>(stream)),
-                    "minf_sparse_attn launch");
+                    what);
+}
+
+minf_status minf_sparse_attn(const minf_problem* prob, const minf_head_cfg* heads, const void* Q, const void* K,
+                             const void* V, const int32_t* blk_idx, const int32_t* blk_cnt, const minf_tiles* tiles,
+                             void* O, float* lse, void* ws, size_t ws_bytes, void* stream) {
+  Derived d;
+  minf_status s = attn_checks(prob, heads, Q, K, V, blk_idx, blk_cnt, tiles, O, &d);
+  if (s != MINF_OK) return s;
+  if ((s = check_ws(prob, d, ws, ws_bytes)) != MINF_OK) return s;
+  return attn_launch(prob, d, Q, K, V, blk_idx, blk_cnt, tiles, O, lse, static_cast<char*>(ws), stream,
+                     "minf_sparse_attn launch");
+}
+
+minf_status minf_sparse_attn_static(const minf_problem* prob, const minf_head_cfg* heads, const void* Q,
+                                    const void* K, const void* V, const int32_t* blk_idx, const int32_t* blk_cnt,
+                                    const minf_tiles* tiles, void* O, float* lse, void* stream) {
+  Derived d;
+  minf_status s = attn_checks(prob, heads, Q, K, V, blk_idx, blk_cnt, tiles, O, &d);
+  if (s != MINF_OK) return s;
+  const size_t need = attn_ws(prob, d).total;
+  if (need > kScratchBytes)
+    return fail(MINF_EWORKSPACE, "minf_sparse_attn_static: the problem needs %zu bytes of scratch, the static scratch "
+                "holds %zu (use minf_sparse_attn with a workspace)", need, kScratchBytes);
+  char* wb = nullptr;
+  if ((s = scratch_on_current_device(&wb)) != MINF_OK) return s;
+  return attn_launch(prob, d, Q, K, V, blk_idx, blk_cnt, tiles, O, lse, wb, stream, "minf_sparse_attn_static launch");
 }
 
 // ---- ragged batches: one workspace holds, for a single sequence of the

@@ -133,6 +133,23 @@ def test_calls_reject_before_launch(lib):
     assert st == M.MINF_EINVAL and "slash_bits" in lib.minf_last_error().decode()
 
 
+def test_static_attention_refuses_oversized_problems(lib):
+    """minf_sparse_attn_static keeps its scheduler scratch in a fixed 8 MiB
+    device array: a problem needing more is refused before any GPU call (the
+    fake pointers are never dereferenced)."""
+    p = _prob(B=64, Hq=64, Hkv=8, n=1 << 20)
+    h = M.make_heads([gen.ashape(16, 100)] * 64)
+    fake = 0x1000
+    ts = M.MinfTiles()
+    st = lib.minf_sparse_attn_static(ctypes.byref(p), h, fake, fake, fake, None, None, ctypes.byref(ts), fake, None,
+                                     None)
+    assert st == M.MINF_EWORKSPACE
+    assert "scratch" in lib.minf_last_error().decode()
+    st = lib.minf_sparse_attn_static(ctypes.byref(_prob()), M.make_heads(HEADS), None, fake, fake, fake, fake,
+                                     ctypes.byref(ts), fake, None, None)
+    assert st == M.MINF_EINVAL
+
+
 def test_no_work_for_absent_kinds(lib):
     """A layer without VS heads makes minf_vs_index a no-op that succeeds
     (and the same for BS); nothing is queued, so no GPU is needed."""
