@@ -36,9 +36,9 @@ PEAK_HBM_GBS = 8000.0            # MI355X HBM3E
 ATTN_KERNEL = "attn_bf16_d128_kernel"
 ATTN_SOURCES = ["long_context_prefill_amd/csrc/attn_bf16.hip", "long_context_prefill_amd/csrc/common.h",
                 "long_context_prefill_amd/csrc/kernels.h", "include/minf.h"]
-ATTN_TRAFFIC = {"workload": "n128k_h32kv8_d128_bf16_mixed", "sources": "e34c5743a6965681",
-                "fetch_kib": 18758445.27, "fetch_factor": 1048576 / 524304.54,
-                "write_kib": 2108089.26, "write_factor": 1048576 / 1048576.0}
+ATTN_TRAFFIC = {"workload": "n128k_h32kv8_d128_bf16_mixed", "sources": "3f1d5a857c337c71",
+                "fetch_kib": 30668146.79, "fetch_factor": 1048576 / 524302.40,
+                "write_kib": 2109175.80, "write_factor": 1048576 / 1048576.0}
 
 
 def log(*a):
