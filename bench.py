@@ -325,7 +325,7 @@ def ragged_batch(a):
     O_r = torch.empty(Hq * T * dh, dtype=torch.float32, device="cuda")
     kept_r = torch.zeros((len(lens), Hq), dtype=torch.int64, device="cuda")
     status = torch.zeros(1, dtype=torch.int32, device="cuda")
-    ws_r = torch.empty(M.minf_ragged_ws_bytes(prob_r, heads), dtype=torch.uint8, device="cuda")
+    ws_r = torch.empty(M.minf_ragged_ws_bytes(prob_r, heads, lens), dtype=torch.uint8, device="cuda")
     stream = torch.cuda.current_stream()
 
     def timed(fn, steps):

@@ -309,18 +309,23 @@ minf_status minf_captured_mass(const minf_problem* prob, const float* lse, const
  *   K, V: [Hkv, len_b, dh] at element offset Hkv*dh*t_b,
  *   lse:  [Hq, len_b] at offset Hq*t_b (fp32; NULL to skip),
  * so the full tensors hold Hq*dh*sum(len) (resp. Hkv*dh*sum(len)) elements.
- * Each sample runs the whole path (minf_vs_index, minf_bs_index,
- * minf_build_tiles, minf_sparse_attn) as a problem of its own length with
- * B = 1, on `stream`, one after another: indices are per sample and no
- * window, slash or block crosses a sample boundary.
+ * The index and tile stages (minf_vs_index, minf_bs_index,
+ * minf_build_tiles) run for each sample as a problem of its own length with
+ * B = 1, one after another on `stream`; then the sparse attention of every
+ * sample runs in ONE launch, whose work items (sample, head, query block)
+ * are scheduled together.  Indices are per sample, and no window, slash or
+ * block crosses a sample boundary.
  *   kept_edges: device [B, Hq] int64, E_h of each sample and head, or NULL;
  *   status: device int32[1], zeroed by the call, then the OR of MINF_DEV_*
  *     bits over all samples;
- *   ws: device workspace of at least minf_ragged_ws_bytes(prob, heads)
- *     bytes (index and tile buffers plus the stage workspace, all for one
- *     sequence of length prob->n, reused by every sample).
- * Errors as for the four calls; MINF_EINVAL for a length outside [1, n]. */
-minf_status minf_ragged_ws_bytes(const minf_problem* prob, const minf_head_cfg* heads, int64_t* ws_bytes);
+ *   ws: device workspace of at least minf_ragged_ws_bytes(prob, heads,
+ *     seq_lens) bytes: every sample's index and tile buffers, one stage
+ *     workspace the samples reuse in turn, the batch's attention schedule
+ *     and a table of per-sample descriptors.
+ * Errors as for the four calls; MINF_EINVAL for a null seq_lens or a length
+ * outside [1, n]. */
+minf_status minf_ragged_ws_bytes(const minf_problem* prob, const minf_head_cfg* heads, const int32_t* seq_lens,
+                                 int64_t* ws_bytes);
 minf_status minf_prefill_ragged(const minf_problem* prob, const minf_head_cfg* heads, const int32_t* seq_lens,
                                 const void* Q, const void* K, const void* V, void* O, float* lse,
                                 int64_t* kept_edges, int32_t* status, void* ws, size_t ws_bytes, void* stream);

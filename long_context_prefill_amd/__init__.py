@@ -16,7 +16,7 @@ Entry points (same names and argument order as include/minf.h):
     minf_sparse_attn_static(...)  the same without a workspace (static scratch)
     minf_output_error(prob, O, O_ref, err, stream=None)
     minf_captured_mass(prob, lse, lse_ref, mass, stream=None)
-    minf_ragged_ws_bytes(prob, heads) -> int
+    minf_ragged_ws_bytes(prob, heads, seq_lens) -> int
     minf_prefill_ragged(prob, heads, seq_lens, Q, K, V, O, lse, kept_edges, status, ws, stream=None)
 The offline pattern search that drives them on calibration input is in
 long_context_prefill_amd.search.
@@ -101,7 +101,7 @@ def load_library(path: str = LIB_PATH):
                                             vp, vp]
     lib.minf_output_error.argtypes = [P(MinfProblem), vp, vp, vp, vp]
     lib.minf_captured_mass.argtypes = [P(MinfProblem), vp, vp, vp, vp]
-    lib.minf_ragged_ws_bytes.argtypes = [P(MinfProblem), P(MinfHeadCfg), P(ctypes.c_int64)]
+    lib.minf_ragged_ws_bytes.argtypes = [P(MinfProblem), P(MinfHeadCfg), P(ctypes.c_int32), P(ctypes.c_int64)]
     lib.minf_prefill_ragged.argtypes = [P(MinfProblem), P(MinfHeadCfg), P(ctypes.c_int32), vp, vp, vp, vp, vp, vp, vp,
                                         vp, ctypes.c_size_t, vp]
     for f in ("minf_query_sizes", "minf_vs_index", "minf_vs_index_fused", "minf_bs_index", "minf_build_tiles",
@@ -239,10 +239,15 @@ def minf_captured_mass(prob, lse, lse_ref, mass, stream=None):
     _check(lib.minf_captured_mass(ctypes.byref(prob), _ptr(lse), _ptr(lse_ref), _ptr(mass), _stream(stream)))
 
 
-def minf_ragged_ws_bytes(prob, heads) -> int:
+def _lens(seq_lens):
+    return (ctypes.c_int32 * max(1, len(seq_lens)))(*[int(x) for x in seq_lens])
+
+
+def minf_ragged_ws_bytes(prob, heads, seq_lens) -> int:
+    """seq_lens: a host sequence of prob.B lengths."""
     lib = load_library()
     out = ctypes.c_int64(0)
-    _check(lib.minf_ragged_ws_bytes(ctypes.byref(prob), heads, ctypes.byref(out)))
+    _check(lib.minf_ragged_ws_bytes(ctypes.byref(prob), heads, _lens(seq_lens), ctypes.byref(out)))
     return int(out.value)
 
 
@@ -250,8 +255,7 @@ def minf_prefill_ragged(prob, heads, seq_lens, Q, K, V, O, lse, kept_edges, stat
     """seq_lens: a host sequence of prob.B lengths; tensors packed as
     include/minf.h describes."""
     lib = load_library()
-    lens = (ctypes.c_int32 * max(1, len(seq_lens)))(*[int(x) for x in seq_lens])
-    _check(lib.minf_prefill_ragged(ctypes.byref(prob), heads, lens, _ptr(Q), _ptr(K), _ptr(V), _ptr(O), _ptr(lse),
+    _check(lib.minf_prefill_ragged(ctypes.byref(prob), heads, _lens(seq_lens), _ptr(Q), _ptr(K), _ptr(V), _ptr(O), _ptr(lse),
                                    _ptr(kept_edges), _ptr(status), _ptr(ws), _nbytes(ws), _stream(stream)))
 
 

@@ -168,14 +168,16 @@ __global__ __launch_bounds__(256, 1) void attn_kernel(AttnParams P) {
   const int utile = P.n_utiles - 1 - (t2 % P.n_utiles);
   const int u = utile * 8 + within / P.gsz;
   const int h = kvg * P.gsz + within % P.gsz;
-  if (u >= P.nq) return;
+  const SampleView SV = sample_view(P, b);
+  if (u >= SV.nq) return;
 
-  const int n = P.n;
+  const int n = SV.n;
   const int kind = __builtin_amdgcn_readfirstlane(P.ht.kind[h]);
   const int row0 = 64 * u;
-  const size_t bh = (size_t)b * P.Hq + h;
-  const T* __restrict__ Qb = reinterpret_cast<const T*>(P.Q) + bh * (size_t)n * DH;
-  const size_t kvoff = ((size_t)b * P.Hkv + kvg) * (size_t)n * DH;
+  const int64_t hrow = SV.q0 + (int64_t)h * n;     // this head's first row in Q, O and lse
+  const int64_t hu = (int64_t)h * SV.nq + u;
+  const T* __restrict__ Qb = reinterpret_cast<const T*>(P.Q) + hrow * DH;
+  const size_t kvoff = (size_t)(SV.kv0 + (int64_t)kvg * n) * DH;
   const T* __restrict__ Kb = reinterpret_cast<const T*>(P.K) + kvoff;
   const T* __restrict__ Vb = reinterpret_cast<const T*>(P.V) + kvoff;
 
@@ -215,15 +217,15 @@ __global__ __launch_bounds__(256, 1) void attn_kernel(AttnParams P) {
     }
   } else if (kind == MINF_VSLASH) {
     // counts are clamped to the capacities so that no list is read past its end
-    Ca = min((long long)max(P.chunk_cnt[bh * P.nq + u], 0), (long long)P.max_chunks);
-    ncols = min((long long)max(P.col_cnt[bh * P.nq + u], 0), (long long)P.max_v);
+    Ca = min((long long)max(SV.chunk_cnt[hu], 0), (long long)SV.max_chunks);
+    ncols = min((long long)max(SV.col_cnt[hu], 0), (long long)SV.max_v);
     Cb = (ncols + 31) >> 5;
-    colrow = P.cols + (bh * P.nq + u) * P.max_v;
-    clo = P.chunk_lo + bh * P.max_chunks;
-    chi = P.chunk_hi + bh * P.max_chunks;
+    colrow = SV.cols + hu * SV.max_v;
+    clo = SV.chunk_lo + (int64_t)h * SV.max_chunks;
+    chi = SV.chunk_hi + (int64_t)h * SV.max_chunks;
   } else {
-    Ca = 2 * (int)min((long long)max(P.blk_cnt[bh * P.nq + u], 0), (long long)P.max_kb);
-    blkrow = P.blk_idx + (bh * P.nq + u) * P.max_kb;
+    Ca = 2 * (int)min((long long)max(SV.blk_cnt[hu], 0), (long long)SV.max_kb);
+    blkrow = SV.blk_idx + hu * SV.max_kb;
   }
   // all of these are wave-uniform; keep them in scalar registers
   Ca = __builtin_amdgcn_readfirstlane(Ca);
@@ -336,8 +338,8 @@ __global__ __launch_bounds__(256, 1) void attn_kernel(AttnParams P) {
           // selected column (bitmaps from the tile stage)
           const int key = kb0 + o;
           const int bs = n + kBitsPad - 1 - (row - key), bc = key + kBitsPad;
-          const uint32_t* sw = P.slash_bits + bh * P.bits_words;
-          const uint32_t* cw = P.col_bits + bh * P.bits_words;
+          const uint32_t* sw = SV.slash_bits + (int64_t)h * SV.bits_words;
+          const uint32_t* cw = SV.col_bits + (int64_t)h * SV.bits_words;
           keep = ((sw[bs >> 5] >> (bs & 31)) & 1u) || ((cw[bc >> 5] >> (bc & 31)) & 1u);
         }
         if (!keep) s[e >> 2][nb][e & 3] = kNegInf;
@@ -545,7 +547,7 @@ __global__ __launch_bounds__(256, 1) void attn_kernel(AttnParams P) {
     }
     if (wave == 0 && g == 0 && P.lse) {
       const int row = row0 + r;
-      if (row < n) P.lse[bh * n + row] = (L > 0.f) ? (M + __log2f(L)) * kLn2 : kNegInf;
+      if (row < n) P.lse[hrow + row] = (L > 0.f) ? (M + __log2f(L)) * kLn2 : kNegInf;
     }
   }
   __syncthreads();
@@ -559,7 +561,7 @@ __global__ __launch_bounds__(256, 1) void attn_kernel(AttnParams P) {
     #pragma unroll
     for (int w = 0; w < kWaves; ++w) o += *reinterpret_cast<const floatx4*>(sm_acc + ((size_t)w * 64 + r) * RS + 4 * c4);
     if (row < n) {
-      const size_t off = (bh * n + row) * (size_t)DH + 4 * c4;
+      const size_t off = (size_t)(hrow + row) * DH + 4 * c4;
       if (P.out_bf16) {
         u32x2 pk = {pack_bf16(o[0], o[1]), pack_bf16(o[2], o[3])};
         *reinterpret_cast<u32x2*>(reinterpret_cast<uint16_t*>(P.O) + off) = pk;
@@ -588,6 +590,23 @@ static hipError_t launch_t(const AttnParams& p, hipStream_t st) {
   timing_mark(st, 0);
   hipLaunchKernelGGL((attn_kernel<T, DH>), dim3(grid), dim3(256), smem, st, p);
   timing_mark(st, 1);
+  return hipGetLastError();
+}
+
+__global__ void write_samples_kernel(SampleBatch b) {
+  // one thread per 8-byte word of the descriptors
+  constexpr int W = (int)(sizeof(SampleDesc) / 8);
+  static_assert(sizeof(SampleDesc) % 8 == 0, "SampleDesc is a whole number of 8-byte words");
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= b.count * W) return;
+  reinterpret_cast<uint64_t*>(b.dst)[i] = reinterpret_cast<const uint64_t*>(b.d)[i];
+}
+
+hipError_t launch_write_samples(const SampleBatch& b, hipStream_t st) {
+  constexpr int W = (int)(sizeof(SampleDesc) / 8);
+  const int words = b.count * W;
+  if (words <= 0) return hipSuccess;
+  hipLaunchKernelGGL(write_samples_kernel, dim3((words + 255) / 256), dim3(256), 0, st, b);
   return hipGetLastError();
 }
 

@@ -92,7 +92,7 @@ struct Chunk {
   int flags;
 };
 
-// The chunk lists of one work item (batch/head bh, query block u): Ca chunks
+// The chunk lists of one work item (head h of sequence S, query block u): Ca chunks
 // of the first list (sink, slash spans or selected blocks) and Cb of the
 // second (window or gathered columns).  Shared by the cost pass of the
 // scheduler and the attention kernel.
@@ -104,9 +104,10 @@ struct ItemLists {
   const int32_t* chi;
 };
 
-__device__ __forceinline__ ItemLists item_lists(const AttnParams& P, size_t bh, int h, int kind, int u) {
+__device__ __forceinline__ ItemLists item_lists(const AttnParams& P, const SampleView& S, int h, int kind, int u) {
   ItemLists L{0, 0, 0, 0, -1, 0, 0, nullptr, nullptr, nullptr, nullptr};
-  const int n = P.n, row0 = 64 * u;
+  const int n = S.n, row0 = 64 * u;
+  const int64_t hu = (int64_t)h * S.nq + u;
   if (kind == MINF_ASHAPE) {
     const int gk = P.ht.a[h];
     L.win = P.ht.b[h];
@@ -119,15 +120,15 @@ __device__ __forceinline__ ItemLists item_lists(const AttnParams& P, size_t bh, 
     }
   } else if (kind == MINF_VSLASH) {
     // counts are clamped to the capacities so that no list is read past its end
-    L.Ca = (int)min((long long)max(ld_uniform(P.chunk_cnt, bh * P.nq + u), 0), (long long)P.max_chunks);
-    L.ncols = (int)min((long long)max(ld_uniform(P.col_cnt, bh * P.nq + u), 0), (long long)P.max_v);
+    L.Ca = (int)min((long long)max(ld_uniform(S.chunk_cnt, hu), 0), (long long)S.max_chunks);
+    L.ncols = (int)min((long long)max(ld_uniform(S.col_cnt, hu), 0), (long long)S.max_v);
     L.Cb = (L.ncols + 31) >> 5;
-    L.colrow = P.cols + (bh * P.nq + u) * P.max_v;
-    L.clo = P.chunk_lo + bh * P.max_chunks;
-    L.chi = P.chunk_hi + bh * P.max_chunks;
+    L.colrow = S.cols + hu * S.max_v;
+    L.clo = S.chunk_lo + (int64_t)h * S.max_chunks;
+    L.chi = S.chunk_hi + (int64_t)h * S.max_chunks;
   } else {
-    L.Ca = 2 * (int)min((long long)max(ld_uniform(P.blk_cnt, bh * P.nq + u), 0), (long long)P.max_kb);
-    L.blkrow = P.blk_idx + (bh * P.nq + u) * P.max_kb;
+    L.Ca = 2 * (int)min((long long)max(ld_uniform(S.blk_cnt, hu), 0), (long long)S.max_kb);
+    L.blkrow = S.blk_idx + hu * S.max_kb;
   }
   return L;
 }
@@ -178,7 +179,8 @@ __device__ __forceinline__ int unit_items(const AttnParams& P, int unit, int* u0
   const int bhi = unit / P.sched_P, part = unit % P.sched_P;
   const int h = bhi % P.Hq;
   *u0 = part * P.sched_R;
-  *u1 = min(*u0 + P.sched_R, P.nq);
+  const int nq = P.samples ? P.samples[bhi / P.Hq].nq : P.nq;   // this sequence's blocks
+  *u1 = min(*u0 + P.sched_R, nq);
   *nbs = 1;
   if (*u0 >= *u1) return 0;
   if (P.ht.kind[h] == MINF_BSPARSE) {
@@ -197,11 +199,12 @@ __global__ __launch_bounds__(256) void attn_cost_kernel(AttnParams P) {
   const int bhi = unit / P.sched_P;
   const int b = bhi / P.Hq, h = bhi % P.Hq;
   const int kind = P.ht.kind[h];
+  const SampleView S = sample_view(P, b);
   long long c = 0;
   for (int i = (int)threadIdx.x; i < items; i += 256) {
     const int u = u1 - 1 - i / nbs;
     const int hh = kind == MINF_BSPARSE ? bs_head(P, (h / P.gsz) * P.gsz, i % nbs) : h;
-    const ItemLists L = item_lists(P, (size_t)b * P.Hq + hh, hh, kind, u);
+    const ItemLists L = item_lists(P, S, hh, kind, u);
     c += L.Ca + L.Cb + 2;   // + fixed cost of an item (Q load, output)
   }
   __shared__ long long sh[256];
@@ -370,18 +373,18 @@ __device__ __forceinline__ void wait_copies_and_barrier() {
 
 // One work item: query block u of head (b, h), both waves of the work-group.
 template <int KIND>
-__device__ __forceinline__ void attn_item(const AttnParams& P, const int b, const int h, const int u, const int slot,
+__device__ __forceinline__ void attn_item(const AttnParams& P, const SampleView& S, const int h, const int u,
                                           lds_char* smem) {
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int l32 = lane & 31;
   const int hh = lane >> 5;
-  const int n = P.n;
+  const int n = S.n;
   const int row0 = 64 * u;
   const int rw0 = row0 + 32 * wave;     // this wave's first row
   const int myrow = rw0 + l32;
-  const size_t bh = (size_t)b * P.Hq + h;
-  const size_t kvoff = ((size_t)b * P.Hkv + h / P.gsz) * (size_t)n * kDH;
+  const int64_t hrow = S.q0 + (int64_t)h * n;     // this head's first row in Q, O and lse
+  const size_t kvoff = (size_t)(S.kv0 + (int64_t)(h / P.gsz) * n) * kDH;
   const char* __restrict__ Kb = reinterpret_cast<const char*>(reinterpret_cast<const uint16_t*>(P.K) + kvoff);
   const char* __restrict__ Vb = reinterpret_cast<const char*>(reinterpret_cast<const uint16_t*>(P.V) + kvoff);
 
@@ -389,7 +392,7 @@ __device__ __forceinline__ void attn_item(const AttnParams& P, const int b, cons
   u32x4 q[8];
   {
     const u32x4* qp = reinterpret_cast<const u32x4*>(reinterpret_cast<const uint16_t*>(P.Q) +
-                                                     (bh * n + min(myrow, n - 1)) * (size_t)kDH);
+                                                     (hrow + min(myrow, n - 1)) * (size_t)kDH);
     #pragma unroll
     for (int t = 0; t < 8; ++t) {
       q[t] = qp[2 * t + hh];
@@ -398,14 +401,14 @@ __device__ __forceinline__ void attn_item(const AttnParams& P, const int b, cons
   }
 
   // ---- chunk lists of this item (wave-uniform)
-  const ItemLists L = item_lists(P, bh, h, KIND, u);
+  const ItemLists L = item_lists(P, S, h, KIND, u);
   const int Ca = __builtin_amdgcn_readfirstlane(L.Ca);
   const int Cb = __builtin_amdgcn_readfirstlane(L.Cb);
   const int C = Ca + Cb;
   if (C <= 0) {
     // nothing kept: o = 0, lse = -inf
     if (myrow < n) {
-      const size_t obase = (bh * n + myrow) * (size_t)kDH;
+      const size_t obase = (hrow + myrow) * (size_t)kDH;
       #pragma unroll
       for (int c = 0; c < 4; ++c) {
         const int col = 32 * c + 16 * hh;
@@ -418,7 +421,7 @@ __device__ __forceinline__ void attn_item(const AttnParams& P, const int b, cons
             *reinterpret_cast<floatx4*>(reinterpret_cast<float*>(P.O) + obase + col + 4 * q4) = floatx4{0.f, 0.f, 0.f, 0.f};
         }
       }
-      if (hh == 0 && P.lse) P.lse[bh * n + myrow] = kNegInf;
+      if (hh == 0 && P.lse) P.lse[hrow + myrow] = kNegInf;
     }
     return;
   }
@@ -597,8 +600,8 @@ __device__ __forceinline__ void attn_item(const AttnParams& P, const int b, cons
       // column.  Offset bits: bit n + kBitsPad - 1 - myrow + kstart + p of
       // slash_bits, a 32-bit window of three words the wave reads together;
       // column bits: bit kstart + p + kBitsPad of col_bits.
-      const uint32_t* sw = P.slash_bits + bh * P.bits_words;
-      const uint32_t* cw = P.col_bits + bh * P.bits_words;
+      const uint32_t* sw = S.slash_bits + (int64_t)h * S.bits_words;
+      const uint32_t* cw = S.col_bits + (int64_t)h * S.bits_words;
       const int w0 = (n + kBitsPad - 1 - rlast + d.kstart) >> 5;
       const uint32_t W0 = (uint32_t)ld_uniform((const int32_t*)sw, w0);
       const uint32_t W1 = (uint32_t)ld_uniform((const int32_t*)sw, w0 + 1);
@@ -697,11 +700,14 @@ __device__ __forceinline__ void attn_item(const AttnParams& P, const int b, cons
   //   block (u-1)'s shifted up by 64 keys (measured: 3.8% faster than the
   //   ascending walk at 128K, and equal at 1M);
   // * A-shape: block u's window is block (u+1)'s shifted down by two chunks,
-  //   so the walk starts two chunks further along per dispatch position;
+  //   and a unit's blocks are queued from the last down, so block u starts
+  //   2 (-u mod 128) chunks along: neighbours in a queue read the same keys
+  //   at the same time, and the order depends on the block alone (a
+  //   sequence gives the same bits wherever its items are queued);
   // * Block-Sparse: selected blocks from the last (the diagonal) down
   //   (3.4% faster than ascending at 512K).
   const int step = KIND == MINF_BSPARSE ? -1 : 1;
-  int kc = KIND == MINF_ASHAPE ? (2 * (slot & 127)) % C : (KIND == MINF_BSPARSE ? C - 1 : 0);
+  int kc = KIND == MINF_ASHAPE ? (2 * (-u & 127)) % C : (KIND == MINF_BSPARSE ? C - 1 : 0);
   auto next_of = [&](int k) {
     k += step;
     return k == C ? 0 : (k < 0 ? C - 1 : k);
@@ -848,7 +854,7 @@ __device__ __forceinline__ void attn_item(const AttnParams& P, const int b, cons
   const float l_tot = l_run + __shfl_xor(l_run, 32);
   const float f = l_tot > 0.f ? 1.0f / l_tot : 0.f;
   if (myrow < n) {
-    const size_t obase = (bh * n + myrow) * (size_t)kDH;
+    const size_t obase = (hrow + myrow) * (size_t)kDH;
     #pragma unroll
     for (int mb = 0; mb < 4; ++mb) {
       #pragma unroll
@@ -864,7 +870,7 @@ __device__ __forceinline__ void attn_item(const AttnParams& P, const int b, cons
       }
     }
     if (hh == 0 && P.lse)
-      P.lse[bh * n + myrow] = l_tot > 0.f ? (m_run + __log2f(l_tot)) * kLn2 : kNegInf;
+      P.lse[hrow + myrow] = l_tot > 0.f ? (m_run + __log2f(l_tot)) * kLn2 : kNegInf;
   }
 }
 
@@ -893,9 +899,10 @@ void attn_bf16_d128_kernel(AttnParams P) {
     const int b = bhi / P.Hq;
     const int h = bhi % P.Hq;
     const int kind = __builtin_amdgcn_readfirstlane(P.ht.kind[h]);
-    if (kind == MINF_VSLASH) attn_item<MINF_VSLASH>(P, b, h, u, qi, smem);
-    else if (kind == MINF_BSPARSE) attn_item<MINF_BSPARSE>(P, b, h, u, qi, smem);
-    else attn_item<MINF_ASHAPE>(P, b, h, u, qi, smem);
+    const SampleView S = sample_view(P, b);
+    if (kind == MINF_VSLASH) attn_item<MINF_VSLASH>(P, S, h, u, smem);
+    else if (kind == MINF_BSPARSE) attn_item<MINF_BSPARSE>(P, S, h, u, smem);
+    else attn_item<MINF_ASHAPE>(P, S, h, u, smem);
     __syncthreads();   // the next item reuses the LDS rings
   }
 }

@@ -385,9 +385,13 @@ static minf_status attn_checks(const minf_problem* prob, const minf_head_cfg* he
 }
 
 // The attention launch on a workspace `wb` that holds attn_ws(prob, d).total bytes.
+// With `samples` (device, prob->B descriptors) the batch is ragged: each
+// sequence's lists, length and row offsets come from its descriptor, and
+// blk_idx, blk_cnt and tiles are not read.
 static minf_status attn_launch(const minf_problem* prob, const Derived& d, const void* Q, const void* K, const void* V,
                                const int32_t* blk_idx, const int32_t* blk_cnt, const minf_tiles* tiles, void* O,
-                               float* lse, char* wb, void* stream, const char* what) {
+                               float* lse, char* wb, void* stream, const char* what,
+                               const minf::SampleDesc* samples = nullptr) {
   const AttnWs w = attn_ws(prob, d);
   minf::AttnParams a{};
   a.sched_cost = reinterpret_cast<int64_t*>(wb + w.cost);
@@ -399,10 +403,11 @@ static minf_status attn_launch(const minf_problem* prob, const Derived& d, const
   a.sched_P = w.P; a.sched_R = w.R; a.sched_units = w.units;
   a.Q = Q; a.K = K; a.V = V; a.O = O; a.lse = lse;
   a.blk_idx = blk_idx; a.blk_cnt = blk_cnt;
-  if (d.has_vs) {
+  if (d.has_vs && !samples) {
     a.chunk_lo = tiles->chunk_lo; a.chunk_hi = tiles->chunk_hi; a.chunk_cnt = tiles->chunk_cnt;
     a.cols = tiles->cols; a.col_cnt = tiles->col_cnt;
   }
+  a.samples = samples;
   a.max_kb = d.max_kb; a.max_chunks = d.max_chunks; a.max_v = d.max_v;
   a.B = prob->B; a.Hq = prob->Hq; a.Hkv = prob->Hkv; a.n = prob->n; a.nq = (int)d.nq;
   a.gsz = prob->Hq / prob->Hkv;
@@ -411,7 +416,7 @@ static minf_status attn_launch(const minf_problem* prob, const Derived& d, const
   a.c = d.scale * minf::kLog2e;
   a.out_bf16 = prob->out_dtype == MINF_BF16;
   a.slash_tile = prob->slash_tile;
-  if (d.bits_words > 0) {
+  if (d.bits_words > 0 && !samples) {
     a.slash_bits = tiles->slash_bits;
     a.col_bits = tiles->col_bits;
     a.bits_words = d.bits_words;
@@ -447,39 +452,73 @@ minf_status minf_sparse_attn_static(const minf_problem* prob, const minf_head_cf
   return attn_launch(prob, d, Q, K, V, blk_idx, blk_cnt, tiles, O, lse, wb, stream, "minf_sparse_attn_static launch");
 }
 
-// ---- ragged batches: one workspace holds, for a single sequence of the
-// longest length, the index and tile buffers and the stage workspace; the
-// samples run one after another on the stream and reuse it.
-struct RaggedLayout {
-  size_t vert, slash, blk, blkcnt, span_lo, span_hi, span_cnt, chunk_lo, chunk_hi, chunk_cnt, cols, col_cnt,
-      sbits, cbits, kept, stage, total;
-};
-static minf_status ragged_layout(const minf_problem* prob, const minf_head_cfg* heads, RaggedLayout* L) {
-  minf_problem one = *prob;
-  one.B = 1;
+// ---- ragged batches: the workspace holds every sequence's index and tile
+// buffers (each laid out as for a B = 1 problem of its own length), one stage
+// workspace that the sequences' index and tile stages reuse in turn, the
+// attention schedule of the whole batch and the table of sequence
+// descriptors that the one attention launch reads.
+struct RaggedRegion {
+  size_t vert, slash, blk, blkcnt, span_lo, span_hi, span_cnt, chunk_lo, chunk_hi, chunk_cnt, cols, col_cnt, sbits,
+      cbits;
   Derived d;
-  minf_status s = validate(&one, heads, &d);
+};
+struct RaggedLayout {
+  std::vector<RaggedRegion> r;
+  minf_problem all;     // the batch as one attention problem: B sequences, n = the longest
+  Derived d_all;
+  size_t stage, stage_bytes, attn, table, kept, total;
+};
+static minf_status ragged_layout(const minf_problem* prob, const minf_head_cfg* heads, const int32_t* seq_lens,
+                                 RaggedLayout* L) {
+  g_err[0] = 0;
+  if (!prob || !heads) return fail(MINF_EINVAL, "null problem or head table");
+  if (!seq_lens) return fail(MINF_EINVAL, "null seq_lens");
+  if (prob->B < 1) return fail(MINF_EINVAL, "B must be >= 1 (B=%d)", prob->B);
+  int n_max = 0;
+  for (int b = 0; b < prob->B; ++b) {
+    if (seq_lens[b] < 1 || seq_lens[b] > prob->n)
+      return fail(MINF_EINVAL, "sequence %d has length %d, outside [1, n=%d]", b, seq_lens[b], prob->n);
+    n_max = std::max(n_max, seq_lens[b]);
+  }
+  Carve c;
+  size_t stage = 256;
+  L->r.assign((size_t)prob->B, RaggedRegion{});
+  const size_t Hq = (size_t)prob->Hq;
+  for (int b = 0; b < prob->B; ++b) {
+    minf_problem one = *prob;
+    one.B = 1;
+    one.n = seq_lens[b];
+    RaggedRegion& R = L->r[(size_t)b];
+    minf_status s = validate(&one, heads, &R.d);
+    if (s != MINF_OK) return s;
+    const Derived& d = R.d;
+    const size_t nq = (size_t)d.nq;
+    R.vert = c.take(4 * Hq * std::max<int64_t>(d.max_v, 1));
+    R.slash = c.take(4 * Hq * std::max<int64_t>(d.max_s, 1));
+    R.blk = c.take(4 * Hq * nq * std::max<int64_t>(d.max_kb, 1));
+    R.blkcnt = c.take(4 * Hq * nq);
+    R.span_lo = c.take(4 * Hq * std::max<int64_t>(d.max_s, 1));
+    R.span_hi = c.take(4 * Hq * std::max<int64_t>(d.max_s, 1));
+    R.span_cnt = c.take(4 * Hq);
+    R.chunk_lo = c.take(4 * Hq * std::max<int64_t>(d.max_chunks, 1));
+    R.chunk_hi = c.take(4 * Hq * std::max<int64_t>(d.max_chunks, 1));
+    R.chunk_cnt = c.take(4 * Hq * nq);
+    R.cols = c.take(4 * Hq * nq * std::max<int64_t>(d.max_v, 1));
+    R.col_cnt = c.take(4 * Hq * nq);
+    R.sbits = c.take(4 * Hq * std::max<int64_t>(d.bits_words, 1));
+    R.cbits = c.take(4 * Hq * std::max<int64_t>(d.bits_words, 1));
+    stage = std::max(stage, ws_total(&one, d));
+  }
+  L->all = *prob;
+  L->all.n = n_max;
+  minf_status s = validate(&L->all, heads, &L->d_all);
   if (s != MINF_OK) return s;
-  const size_t Hq = (size_t)prob->Hq, nq = (size_t)d.nq;
-  size_t off = 0;
-  auto take = [&](size_t bytes) { const size_t o = off; off += (bytes + 255) & ~size_t(255); return o; };
-  L->vert = take(4 * Hq * std::max<int64_t>(d.max_v, 1));
-  L->slash = take(4 * Hq * std::max<int64_t>(d.max_s, 1));
-  L->blk = take(4 * Hq * nq * std::max<int64_t>(d.max_kb, 1));
-  L->blkcnt = take(4 * Hq * nq);
-  L->span_lo = take(4 * Hq * std::max<int64_t>(d.max_s, 1));
-  L->span_hi = take(4 * Hq * std::max<int64_t>(d.max_s, 1));
-  L->span_cnt = take(4 * Hq);
-  L->chunk_lo = take(4 * Hq * std::max<int64_t>(d.max_chunks, 1));
-  L->chunk_hi = take(4 * Hq * std::max<int64_t>(d.max_chunks, 1));
-  L->chunk_cnt = take(4 * Hq * nq);
-  L->cols = take(4 * Hq * nq * std::max<int64_t>(d.max_v, 1));
-  L->col_cnt = take(4 * Hq * nq);
-  L->sbits = take(4 * Hq * std::max<int64_t>(d.bits_words, 1));
-  L->cbits = take(4 * Hq * std::max<int64_t>(d.bits_words, 1));
-  L->kept = take(8 * Hq);
-  L->stage = take(ws_total(&one, d));
-  L->total = off;
+  L->stage_bytes = stage;
+  L->stage = c.take(stage);
+  L->attn = c.take(attn_ws(&L->all, L->d_all).total);
+  L->table = c.take(sizeof(minf::SampleDesc) * (size_t)prob->B);
+  L->kept = c.take(8 * Hq);
+  L->total = c.off;
   return MINF_OK;
 }
 
@@ -509,11 +548,12 @@ minf_status minf_captured_mass(const minf_problem* prob, const float* lse, const
                     "minf_captured_mass launch");
 }
 
-minf_status minf_ragged_ws_bytes(const minf_problem* prob, const minf_head_cfg* heads, int64_t* ws_bytes) {
+minf_status minf_ragged_ws_bytes(const minf_problem* prob, const minf_head_cfg* heads, const int32_t* seq_lens,
+                                 int64_t* ws_bytes) {
   g_err[0] = 0;
   if (!ws_bytes) return fail(MINF_EINVAL, "null ws_bytes");
   RaggedLayout L;
-  const minf_status s = ragged_layout(prob, heads, &L);
+  const minf_status s = ragged_layout(prob, heads, seq_lens, &L);
   if (s != MINF_OK) return s;
   *ws_bytes = (int64_t)L.total;
   return MINF_OK;
@@ -524,59 +564,79 @@ minf_status minf_prefill_ragged(const minf_problem* prob, const minf_head_cfg* h
                                 int64_t* kept_edges, int32_t* status, void* ws, size_t ws_bytes, void* stream) {
   g_err[0] = 0;
   RaggedLayout L;
-  minf_status s = ragged_layout(prob, heads, &L);
+  minf_status s = ragged_layout(prob, heads, seq_lens, &L);
   if (s != MINF_OK) return s;
-  if (!seq_lens || !Q || !K || !V || !O || !status) return fail(MINF_EINVAL, "null seq_lens, Q, K, V, O or status");
-  for (int b = 0; b < prob->B; ++b)
-    if (seq_lens[b] < 1 || seq_lens[b] > prob->n)
-      return fail(MINF_EINVAL, "sequence %d has length %d, outside [1, n=%d]", b, seq_lens[b], prob->n);
+  if (!Q || !K || !V || !O || !status) return fail(MINF_EINVAL, "null Q, K, V, O or status");
   if (!ws) return fail(MINF_EWORKSPACE, "workspace pointer is null");
   if (ws_bytes < L.total) return fail(MINF_EWORKSPACE, "workspace of %zu bytes is smaller than the %zu needed", ws_bytes,
                                       L.total);
   hipStream_t st = static_cast<hipStream_t>(stream);
   if ((s = hip_status(minf::launch_fill_i32(status, 1, 0, st), "status reset")) != MINF_OK) return s;
   char* w = static_cast<char*>(ws);
-  const size_t in_sz = prob->in_dtype == MINF_BF16 ? 2 : 4, out_sz = prob->out_dtype == MINF_BF16 ? 2 : 4;
+  const size_t in_sz = prob->in_dtype == MINF_BF16 ? 2 : 4;
   const size_t Hq = (size_t)prob->Hq, Hkv = (size_t)prob->Hkv, dh = (size_t)prob->dh;
+  minf::SampleDesc* table = reinterpret_cast<minf::SampleDesc*>(w + L.table);
+  minf::SampleBatch batch{};
+  int in_batch = 0;
   size_t off = 0;   // tokens before sample b
+  // index and tile stages, one sequence after another (each a B = 1
+  // problem of its own length, into its own region); the descriptors of the
+  // sequences go to the table in batches
   for (int b = 0; b < prob->B; ++b) {
+    const RaggedRegion& R = L.r[(size_t)b];
     minf_problem one = *prob;
     one.B = 1;
     one.n = seq_lens[b];
     minf_tiles t{};
-    t.span_lo = reinterpret_cast<int32_t*>(w + L.span_lo);
-    t.span_hi = reinterpret_cast<int32_t*>(w + L.span_hi);
-    t.span_cnt = reinterpret_cast<int32_t*>(w + L.span_cnt);
-    t.chunk_lo = reinterpret_cast<int32_t*>(w + L.chunk_lo);
-    t.chunk_hi = reinterpret_cast<int32_t*>(w + L.chunk_hi);
-    t.chunk_cnt = reinterpret_cast<int32_t*>(w + L.chunk_cnt);
-    t.cols = reinterpret_cast<int32_t*>(w + L.cols);
-    t.col_cnt = reinterpret_cast<int32_t*>(w + L.col_cnt);
-    t.slash_bits = reinterpret_cast<uint32_t*>(w + L.sbits);
-    t.col_bits = reinterpret_cast<uint32_t*>(w + L.cbits);
+    t.span_lo = reinterpret_cast<int32_t*>(w + R.span_lo);
+    t.span_hi = reinterpret_cast<int32_t*>(w + R.span_hi);
+    t.span_cnt = reinterpret_cast<int32_t*>(w + R.span_cnt);
+    t.chunk_lo = reinterpret_cast<int32_t*>(w + R.chunk_lo);
+    t.chunk_hi = reinterpret_cast<int32_t*>(w + R.chunk_hi);
+    t.chunk_cnt = reinterpret_cast<int32_t*>(w + R.chunk_cnt);
+    t.cols = reinterpret_cast<int32_t*>(w + R.cols);
+    t.col_cnt = reinterpret_cast<int32_t*>(w + R.col_cnt);
+    t.slash_bits = reinterpret_cast<uint32_t*>(w + R.sbits);
+    t.col_bits = reinterpret_cast<uint32_t*>(w + R.cbits);
     t.status = status;
     // kept edges of this sample go straight to the caller's [B, Hq] array,
     // or to a scratch row of the workspace
     t.kept_edges = kept_edges ? kept_edges + (size_t)b * Hq : reinterpret_cast<int64_t*>(w + L.kept);
-    int32_t* vert = reinterpret_cast<int32_t*>(w + L.vert);
-    int32_t* slash = reinterpret_cast<int32_t*>(w + L.slash);
-    int32_t* blk = reinterpret_cast<int32_t*>(w + L.blk);
-    int32_t* blkcnt = reinterpret_cast<int32_t*>(w + L.blkcnt);
+    int32_t* vert = reinterpret_cast<int32_t*>(w + R.vert);
+    int32_t* slash = reinterpret_cast<int32_t*>(w + R.slash);
+    int32_t* blk = reinterpret_cast<int32_t*>(w + R.blk);
+    int32_t* blkcnt = reinterpret_cast<int32_t*>(w + R.blkcnt);
     void* stage = w + L.stage;
-    const size_t stage_bytes = L.total - L.stage;
     const char* Qb = static_cast<const char*>(Q) + in_sz * Hq * dh * off;
     const char* Kb = static_cast<const char*>(K) + in_sz * Hkv * dh * off;
-    const char* Vb = static_cast<const char*>(V) + in_sz * Hkv * dh * off;
-    char* Ob = static_cast<char*>(O) + out_sz * Hq * dh * off;
-    float* lb = lse ? lse + Hq * off : nullptr;
-    if ((s = minf_vs_index(&one, heads, Qb, Kb, vert, slash, nullptr, nullptr, stage, stage_bytes, stream)) != MINF_OK ||
-        (s = minf_bs_index(&one, heads, Qb, Kb, blk, blkcnt, stage, stage_bytes, stream)) != MINF_OK ||
-        (s = minf_build_tiles(&one, heads, vert, slash, blk, blkcnt, &t, stage, stage_bytes, stream)) != MINF_OK ||
-        (s = minf_sparse_attn(&one, heads, Qb, Kb, Vb, blk, blkcnt, &t, Ob, lb, stage, stage_bytes, stream)) != MINF_OK)
+    if ((s = minf_vs_index(&one, heads, Qb, Kb, vert, slash, nullptr, nullptr, stage, L.stage_bytes, stream)) != MINF_OK ||
+        (s = minf_bs_index(&one, heads, Qb, Kb, blk, blkcnt, stage, L.stage_bytes, stream)) != MINF_OK ||
+        (s = minf_build_tiles(&one, heads, vert, slash, blk, blkcnt, &t, stage, L.stage_bytes, stream)) != MINF_OK)
       return s;
+    minf::SampleDesc& D = batch.d[in_batch++];
+    D = minf::SampleDesc{};
+    D.q_row = (int64_t)(Hq * off);
+    D.kv_row = (int64_t)(Hkv * off);
+    D.chunk_lo = t.chunk_lo; D.chunk_hi = t.chunk_hi; D.chunk_cnt = t.chunk_cnt;
+    D.cols = t.cols; D.col_cnt = t.col_cnt;
+    D.blk_idx = blk; D.blk_cnt = blkcnt;
+    D.slash_bits = R.d.bits_words > 0 ? t.slash_bits : nullptr;
+    D.col_bits = R.d.bits_words > 0 ? t.col_bits : nullptr;
+    D.max_chunks = R.d.max_chunks; D.max_v = R.d.max_v; D.max_kb = R.d.max_kb; D.bits_words = R.d.bits_words;
+    D.n = seq_lens[b];
+    D.nq = (int32_t)R.d.nq;
+    if (in_batch == minf::kSampleBatch || b + 1 == prob->B) {
+      batch.dst = table + (b + 1 - in_batch);
+      batch.count = in_batch;
+      if ((s = hip_status(minf::launch_write_samples(batch, st), "sequence table")) != MINF_OK) return s;
+      in_batch = 0;
+    }
     off += (size_t)seq_lens[b];
   }
-  return MINF_OK;
+  // the attention of every sequence in one launch
+  minf_tiles none{};
+  return attn_launch(&L.all, L.d_all, Q, K, V, nullptr, nullptr, &none, O, lse, w + L.attn, stream,
+                     "minf_prefill_ragged attention launch", table);
 }
 
 minf_status minf_timing_start(int32_t max_calls) {

@@ -13,6 +13,35 @@ constexpr int kBitsPad = 128;
 inline int64_t exact_bits_words(int n) { return ((int64_t)n + 2 * kBitsPad + 64 + 31) / 32 + 2; }
 
 // ---------------------------------------------------------------- attention
+// One sequence of a ragged batch, as the attention kernels see it: its
+// length, where its rows start in the packed Q, K, V, O and lse tensors, and
+// its own index and tile lists (each laid out as for a B = 1 problem of
+// length n, with that problem's capacities).
+struct SampleDesc {
+  int64_t q_row;        // first row of the sample's [Hq, n] rows of Q, O and lse (rows of dh elements in Q, O)
+  int64_t kv_row;       // first row of its [Hkv, n] rows of K and V
+  const int32_t* chunk_lo;
+  const int32_t* chunk_hi;
+  const int32_t* chunk_cnt;
+  const int32_t* cols;
+  const int32_t* col_cnt;
+  const int32_t* blk_idx;
+  const int32_t* blk_cnt;
+  const uint32_t* slash_bits;
+  const uint32_t* col_bits;
+  int64_t max_chunks, max_v, max_kb, bits_words;
+  int32_t n, nq;
+};
+constexpr int kSampleBatch = 16;     // descriptors written per launch of the table writer
+struct SampleBatch {
+  SampleDesc d[kSampleBatch];
+  SampleDesc* dst;
+  int32_t count;
+};
+// dst[0 .. count) = d[0 .. count) (attn.hip), a plain kernel, so that the
+// table needs no host-to-device copy.
+hipError_t launch_write_samples(const SampleBatch& b, hipStream_t st);
+
 struct AttnParams {
   const void* Q;
   const void* K;
@@ -46,7 +75,57 @@ struct AttnParams {
   const uint32_t* slash_bits;   // [B,Hq,bits_words]: bit n + kBitsPad - 1 - d set iff d in D_h
   const uint32_t* col_bits;     // [B,Hq,bits_words]: bit j + kBitsPad set iff j in C_h
   int64_t bits_words;
+  // ragged batch: B sequences described by samples[B] (device); the fields
+  // above that describe lists, lengths and capacities are then unused, except
+  // n and nq, which hold the longest sequence's (they size the schedule and
+  // split queue entries).  nullptr: B sequences of length n, lists as above.
+  const SampleDesc* samples;
 };
+
+// Sequence b of an attention launch, whichever way the batch is given:
+// bases of head 0 of the sequence and its sizes.  Wave-uniform.
+struct SampleView {
+  int n, nq;
+  int64_t q0, kv0;         // first row of head 0 in Q, O and lse; in K and V
+  const int32_t* chunk_lo;
+  const int32_t* chunk_hi;
+  const int32_t* chunk_cnt;
+  const int32_t* cols;
+  const int32_t* col_cnt;
+  const int32_t* blk_idx;
+  const int32_t* blk_cnt;
+  const uint32_t* slash_bits;
+  const uint32_t* col_bits;
+  int64_t max_chunks, max_v, max_kb, bits_words;
+};
+__device__ __forceinline__ SampleView sample_view(const AttnParams& P, int b) {
+  SampleView v;
+  if (P.samples) {
+    const SampleDesc* d = P.samples + b;
+    v.n = d->n; v.nq = d->nq;
+    v.q0 = d->q_row; v.kv0 = d->kv_row;
+    v.chunk_lo = d->chunk_lo; v.chunk_hi = d->chunk_hi; v.chunk_cnt = d->chunk_cnt;
+    v.cols = d->cols; v.col_cnt = d->col_cnt; v.blk_idx = d->blk_idx; v.blk_cnt = d->blk_cnt;
+    v.slash_bits = d->slash_bits; v.col_bits = d->col_bits;
+    v.max_chunks = d->max_chunks; v.max_v = d->max_v; v.max_kb = d->max_kb; v.bits_words = d->bits_words;
+  } else {
+    const int64_t bq = (int64_t)b * P.Hq;
+    v.n = P.n; v.nq = P.nq;
+    v.q0 = bq * (int64_t)P.n;
+    v.kv0 = (int64_t)b * P.Hkv * (int64_t)P.n;
+    v.chunk_lo = P.chunk_lo ? P.chunk_lo + bq * P.max_chunks : nullptr;
+    v.chunk_hi = P.chunk_hi ? P.chunk_hi + bq * P.max_chunks : nullptr;
+    v.chunk_cnt = P.chunk_cnt ? P.chunk_cnt + bq * P.nq : nullptr;
+    v.cols = P.cols ? P.cols + bq * P.nq * P.max_v : nullptr;
+    v.col_cnt = P.col_cnt ? P.col_cnt + bq * P.nq : nullptr;
+    v.blk_idx = P.blk_idx ? P.blk_idx + bq * P.nq * P.max_kb : nullptr;
+    v.blk_cnt = P.blk_cnt ? P.blk_cnt + bq * P.nq : nullptr;
+    v.slash_bits = P.slash_bits ? P.slash_bits + bq * P.bits_words : nullptr;
+    v.col_bits = P.col_bits ? P.col_bits + bq * P.bits_words : nullptr;
+    v.max_chunks = P.max_chunks; v.max_v = P.max_v; v.max_kb = P.max_kb; v.bits_words = P.bits_words;
+  }
+  return v;
+}
 // Units of the bf16 attention schedule: each head's query blocks are cut
 // into P runs of R consecutive blocks.  About kUnitsPerGroup units per KV
 // group, so that one group's work spreads evenly over the eight XCD queues

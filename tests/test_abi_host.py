@@ -191,9 +191,15 @@ def test_ragged_rejects_bad_arguments(lib):
     fake = 0x1000
     p = _prob(B=3)
     h = M.make_heads(HEADS)
-    need = M.minf_ragged_ws_bytes(p, h)
+    need = M.minf_ragged_ws_bytes(p, h, [10, 1000, 7])
     one = M.minf_query_sizes(_prob(B=1), h)
     assert need >= one.ws_bytes
+    # the workspace grows with the lengths (every sample keeps its own lists)
+    assert M.minf_ragged_ws_bytes(p, h, [10, 20, 7]) < need
+    out = ctypes.c_int64(0)
+    assert lib.minf_ragged_ws_bytes(ctypes.byref(p), h, None, ctypes.byref(out)) == M.MINF_EINVAL
+    assert lib.minf_ragged_ws_bytes(ctypes.byref(p), h, (ctypes.c_int32 * 3)(10, 1001, 7),
+                                    ctypes.byref(out)) == M.MINF_EINVAL
     def call(lens, Q=fake, O=fake, status=fake, ws=fake, ws_bytes=need):
         arr = None if lens is None else (ctypes.c_int32 * len(lens))(*lens)
         return lib.minf_prefill_ragged(ctypes.byref(p), h, arr, Q, fake, fake, O, None, None, status, ws, ws_bytes,

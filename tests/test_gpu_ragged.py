@@ -3,7 +3,8 @@
 of different lengths, no padding), with per-sample indices and no window,
 slash or block crossing a sample boundary.
 
-* every sample of a packed batch equals, bit for bit, the same sample run
+* every sample of a packed batch, whose attention runs in one launch over
+  the work items of all samples, equals, bit for bit, the same sample run
   alone through the four calls (minf_vs_index, minf_bs_index,
   minf_build_tiles, minf_sparse_attn), kept edges included;
 * changing one sample's data leaves every other sample's output unchanged;
@@ -57,7 +58,7 @@ def _run_ragged(samples, heads_cfg, n_max, dtype):
     lse = torch.full((s0.Hq * T,), float("nan"), dtype=torch.float32, device="cuda")
     kept = torch.full((len(samples), s0.Hq), -1, dtype=torch.int64, device="cuda")
     status = torch.full((1,), 7, dtype=torch.int32, device="cuda")
-    ws = torch.empty(M.minf_ragged_ws_bytes(prob, heads), dtype=torch.uint8, device="cuda")
+    ws = torch.empty(M.minf_ragged_ws_bytes(prob, heads, lens), dtype=torch.uint8, device="cuda")
     M.minf_prefill_ragged(prob, heads, lens, _dev(Qp, dtype), _dev(Kp, dtype), _dev(Vp, dtype), O_, lse, kept,
                           status, ws)
     torch.cuda.synchronize()
