@@ -58,6 +58,31 @@ __device__ int block_exscan(int x, int* sh, int* total) {
   return before + v - x;
 }
 
+// The list kernels below take kIPT consecutive entries per thread and round
+// (256 kIPT entries per round), with every load of a round issued before its
+// first use, so a round costs one memory latency rather than kIPT.
+constexpr int kIPT = 8;
+constexpr int kRound = 256 * kIPT;
+
+// Last index r in [0, cnt) with a[r] <= x (a ascending), -1 if none, found
+// by one wave: up to 64 sampled entries per step, so a list of up to 4096
+// entries costs two rounds of loads instead of a dependent chain of twelve.
+__device__ __forceinline__ int wave_last_le(const int32_t* a, int cnt, int x) {
+  const int lane = threadIdx.x & 63;
+  int lo = 0, hi = cnt;   // the answer lies in [lo - 1, hi - 1]; a[lo - 1] <= x when lo > 0
+  while (hi - lo > 64) {
+    const int stride = (hi - lo + 63) / 64;
+    const int k = lo + lane * stride;
+    const int c = __popcll(__ballot(k < hi && a[k] <= x));   // sampled entries <= x form a prefix
+    if (c == 0) { hi = lo; break; }
+    const int nlo = lo + (c - 1) * stride;
+    hi = min(hi, nlo + stride);
+    lo = nlo;
+  }
+  const int k = lo + lane;
+  return lo - 1 + __popcll(__ballot(k < hi && a[k] <= x));
+}
+
 // 1) validate indices, initialise kept_edges, merge slash ranges.
 __global__ __launch_bounds__(256) void vs_ranges_kernel(TileParams P) {
   __shared__ int sh[256];
@@ -76,14 +101,25 @@ __global__ __launch_bounds__(256) void vs_ranges_kernel(TileParams P) {
   const int32_t* offs = P.slash_idx + (size_t)bh * P.max_s;
   const int32_t* cols = P.vert_idx + (size_t)bh * P.max_v;
   __syncthreads();
-  for (int k = threadIdx.x; k < ns; k += 256) {
-    const int d = offs[k];
-    if (d < 0 || d >= P.n || (k > 0 && offs[k - 1] >= d)) bad_s = 1;
-  }
-  for (int k = threadIdx.x; k < nv; k += 256) {
-    const int c = cols[k];
-    if (c < 0 || c >= P.n || (k > 0 && cols[k - 1] >= c)) bad_v = 1;
-  }
+  // each list must lie in [0, n) and ascend strictly
+  auto check = [&](const int32_t* a, int cnt, int* bad) {
+    for (int base = 0; base < cnt; base += kRound) {
+      const int k0 = base + (int)threadIdx.x * kIPT;
+      int v[kIPT + 1];   // entries k0 - 1 .. k0 + kIPT - 1
+      #pragma unroll
+      for (int e = 0; e <= kIPT; ++e) {
+        const int k = k0 - 1 + e;
+        v[e] = (k >= 0 && k < cnt) ? a[k] : 0;
+      }
+      #pragma unroll
+      for (int e = 1; e <= kIPT; ++e) {
+        const int k = k0 - 1 + e;
+        if (k < cnt && (v[e] < 0 || v[e] >= P.n || (k > 0 && v[e - 1] >= v[e]))) *bad = 1;
+      }
+    }
+  };
+  check(offs, ns, &bad_s);
+  check(cols, nv, &bad_v);
   __syncthreads();
   const bool ok = !(bad_s || bad_v);
   if (threadIdx.x == 0) {
@@ -92,19 +128,37 @@ __global__ __launch_bounds__(256) void vs_ranges_kernel(TileParams P) {
   }
   int carry = 0;   // ranges emitted so far
   if (ok) {
-    for (int base = 0; base < ns; base += 256) {
-      const int k = base + threadIdx.x;
-      int flag = 0, d = 0;
-      if (k < ns) {
-        d = offs[k];
-        flag = (k == 0) || (d - offs[k - 1] > 64);
+    // offset k starts a range when k = 0 or it lies more than 64 above the
+    // previous one, and ends one when k = ns - 1 or the next lies more than
+    // 64 above it
+    int32_t* slo = P.t.span_lo + (size_t)bh * P.max_s;
+    int32_t* shi = P.t.span_hi + (size_t)bh * P.max_s;
+    for (int base = 0; base < ns; base += kRound) {
+      const int k0 = base + (int)threadIdx.x * kIPT;
+      int v[kIPT + 2];   // entries k0 - 1 .. k0 + kIPT
+      #pragma unroll
+      for (int e = 0; e < kIPT + 2; ++e) {
+        const int k = k0 - 1 + e;
+        v[e] = (k >= 0 && k < ns) ? offs[k] : 0;
+      }
+      int starts = 0;
+      #pragma unroll
+      for (int e = 1; e <= kIPT; ++e) {
+        const int k = k0 - 1 + e;
+        starts += (k < ns) && (k == 0 || v[e] - v[e - 1] > 64);
       }
       int tot;
-      const int pos = carry + block_exscan(flag, sh, &tot);   // index of the new range if flag
-      if (k < ns) {
-        if (flag) P.t.span_lo[(size_t)bh * P.max_s + pos] = d - 63;
-        const bool last = (k == ns - 1) || (offs[k + 1] - d > 64);
-        if (last) P.t.span_hi[(size_t)bh * P.max_s + pos + flag - 1] = d;
+      int pos = carry + block_exscan(starts, sh, &tot);   // ranges started before this thread's entries
+      #pragma unroll
+      for (int e = 1; e <= kIPT; ++e) {
+        const int k = k0 - 1 + e;
+        if (k < ns) {
+          const int flag = (k == 0) || (v[e] - v[e - 1] > 64);
+          if (flag) slo[pos] = v[e] - 63;
+          const bool last = (k == ns - 1) || (v[e + 1] - v[e] > 64);
+          if (last) shi[pos + flag - 1] = v[e];
+          pos += flag;
+        }
       }
       carry += tot;
     }
@@ -112,9 +166,14 @@ __global__ __launch_bounds__(256) void vs_ranges_kernel(TileParams P) {
   if (threadIdx.x == 0) P.t.span_cnt[bh] = ok ? carry : 0;
 }
 
-// 2) cut ranges into chunks, prefix counts, coverage bitmap.
+// 2) cut ranges into chunks, prefix counts, coverage bitmap.  The bitmap is
+//    assembled in LDS, kSlabWords words at a time: a range is at least 64
+//    bits wide, so a word meets at most two ranges and every word is written
+//    once, whole.
+constexpr int kSlabWords = 8192;
 __global__ __launch_bounds__(256) void vs_chunks_kernel(TileParams P) {
   __shared__ int sh[256];
+  __shared__ uint32_t slab[kSlabWords];
   const int bh = blockIdx.x;
   const int h = bh % P.Hq;
   if (P.ht.kind[h] != MINF_VSLASH) return;
@@ -123,51 +182,71 @@ __global__ __launch_bounds__(256) void vs_chunks_kernel(TileParams P) {
   const int32_t* hi = P.t.span_hi + (size_t)bh * P.max_s;
   int32_t* cum = P.span_cum + (size_t)bh * (P.max_s + 1);
   int32_t* rch = P.range_chunks + (size_t)bh * (P.max_s + 1);
+  int32_t* clo = P.t.chunk_lo + (size_t)bh * P.max_chunks;
+  int32_t* chi = P.t.chunk_hi + (size_t)bh * P.max_chunks;
   int carry_c = 0, carry_x = 0;
-  for (int base = 0; base < nr; base += 256) {
-    const int r = base + threadIdx.x;
-    int nch = 0, cov = 0, a = 0, bb = 0;
-    if (r < nr) {
-      a = lo[r]; bb = hi[r];
-      nch = (bb - a + 32) >> 5;
-      cov = bb >= 0 ? bb - max(a, 0) + 1 : 0;
+  for (int base = 0; base < nr; base += kRound) {
+    const int r0 = base + (int)threadIdx.x * kIPT;
+    int a[kIPT], b[kIPT];
+    #pragma unroll
+    for (int e = 0; e < kIPT; ++e) {
+      const int r = r0 + e;
+      a[e] = r < nr ? lo[r] : 0;
+      b[e] = r < nr ? hi[r] : -1;
+    }
+    int sc = 0, sx = 0;
+    #pragma unroll
+    for (int e = 0; e < kIPT; ++e) {
+      if (r0 + e < nr) {
+        sc += (b[e] - a[e] + 32) >> 5;
+        sx += b[e] >= 0 ? b[e] - max(a[e], 0) + 1 : 0;
+      }
     }
     int tc, tx;
-    const int pc = carry_c + block_exscan(nch, sh, &tc);
-    const int px = carry_x + block_exscan(cov, sh, &tx);
-    if (r < nr) {
-      rch[r] = pc;
-      cum[r] = px;
+    int pc = carry_c + block_exscan(sc, sh, &tc);
+    int px = carry_x + block_exscan(sx, sh, &tx);
+    #pragma unroll
+    for (int e = 0; e < kIPT; ++e) {
+      const int r = r0 + e;
+      if (r < nr) {
+        rch[r] = pc;
+        cum[r] = px;
+        // the range's chunks of at most 32 offsets, from its low end
+        const int nch = (b[e] - a[e] + 32) >> 5;
+        for (int m = 0; m < nch; ++m) {
+          const int c = pc + m;
+          if (c < P.max_chunks) {
+            clo[c] = a[e] + 32 * m;
+            chi[c] = min(a[e] + 32 * m + 31, b[e]);
+          }
+        }
+        pc += nch;
+        px += b[e] >= 0 ? b[e] - max(a[e], 0) + 1 : 0;
+      }
     }
     carry_c += tc;
     carry_x += tx;
   }
   if (threadIdx.x == 0) { rch[nr] = carry_c; cum[nr] = carry_x; }
   if (threadIdx.x == 0 && carry_c > P.max_chunks) atomicOr(P.t.status, MINF_DEV_CAPACITY);
-  __syncthreads();
-  // chunk c belongs to the range r with rch[r] <= c < rch[r+1]
-  const int nchunks = min<long long>(carry_c, P.max_chunks);
-  for (int c = threadIdx.x; c < nchunks; c += 256) {
-    int l = 0, rr = nr;   // last r with rch[r] <= c
-    while (rr - l > 1) { const int mid = (l + rr) >> 1; if (rch[mid] <= c) l = mid; else rr = mid; }
-    const int m = c - rch[l];
-    P.t.chunk_lo[(size_t)bh * P.max_chunks + c] = lo[l] + 32 * m;
-    P.t.chunk_hi[(size_t)bh * P.max_chunks + c] = min(lo[l] + 32 * m + 31, hi[l]);
-  }
   // coverage bitmap over x in [-63, n): bit (x + 63)
   uint32_t* bm = P.bitmap + (size_t)bh * P.bm_words;
-  for (int w = threadIdx.x; w < P.bm_words; w += 256) {
-    const int x0 = 32 * w - 63, x1 = x0 + 31;
-    // first range with hi >= x0
-    int l = 0, rr = nr;
-    while (l < rr) { const int mid = (l + rr) >> 1; if (hi[mid] < x0) l = mid + 1; else rr = mid; }
-    uint32_t bits = 0;
-    for (int r = l; r < nr && lo[r] <= x1; ++r) {
-      const int s = max(lo[r], x0) - x0, e = min(hi[r], x1) - x0;
-      const uint32_t span = (e - s + 1 == 32) ? 0xffffffffu : (((1u << (e - s + 1)) - 1u) << s);
-      bits |= span;
+  for (int64_t w0 = 0; w0 < P.bm_words; w0 += kSlabWords) {
+    const int nw = (int)min<int64_t>(kSlabWords, P.bm_words - w0);
+    for (int w = threadIdx.x; w < nw; w += 256) slab[w] = 0u;
+    __syncthreads();
+    const int64_t b0 = 32 * w0, b1 = b0 + 32 * (int64_t)nw - 1;   // bits of this slab
+    for (int r = threadIdx.x; r < nr; r += 256) {
+      const int64_t s = max<int64_t>((int64_t)lo[r] + 63, b0), e = min<int64_t>((int64_t)hi[r] + 63, b1);
+      for (int64_t w = s >> 5; w <= (e >> 5) && s <= e; ++w) {
+        const int64_t ws = max(s, 32 * w) - 32 * w, we = min(e, 32 * w + 31) - 32 * w;
+        const uint32_t span = (we - ws + 1 == 32) ? 0xffffffffu : (((1u << (we - ws + 1)) - 1u) << ws);
+        atomicOr(&slab[w - w0], span);
+      }
     }
-    bm[w] = bits;
+    __syncthreads();
+    for (int w = threadIdx.x; w < nw; w += 256) bm[w0 + w] = slab[w];
+    __syncthreads();   // the slab is cleared again for the next words
   }
 }
 
@@ -177,7 +256,8 @@ __device__ __forceinline__ bool covered(const uint32_t* bm, int x) {
 }
 
 // 3) per query block: chunk count, uncovered verticals, kept edges (VS).
-//    One wave per query block.
+//    One wave per query block; the columns are read four rounds of 64 at a
+//    time, each round's loads (column, then coverage word) issued together.
 __global__ __launch_bounds__(256) void vs_cols_kernel(TileParams P) {
   const int bh = blockIdx.y;
   const int h = bh % P.Hq;
@@ -200,15 +280,14 @@ __global__ __launch_bounds__(256) void vs_cols_kernel(TileParams P) {
     const uint32_t* bm = P.bitmap + (size_t)bh * P.bm_words;
     // last range with lo <= 64u
     const int X = row0;
-    int l = 0, r = nr;
-    while (l < r) { const int mid = (l + r) >> 1; if (lo[mid] <= X) l = mid + 1; else r = mid; }
-    const int rs = l - 1;   // -1 if none
+    const int rs = wave_last_le(lo, nr, X);   // -1 if none
     int ccnt = 0;
     long long cov_pos = 0;  // |S intersect [0, X]|
     if (rs >= 0) {
-      ccnt = rch[rs] + min((hi[rs] - lo[rs] + 32) >> 5, ((X - lo[rs]) >> 5) + 1);
-      const int e = min(hi[rs], X), s = max(lo[rs], 0);
-      cov_pos = cum[rs] + (e >= s ? e - s + 1 : 0);
+      const int l = lo[rs], hh = hi[rs], rc = rch[rs], cu = cum[rs];
+      ccnt = rc + min((hh - l + 32) >> 5, ((X - l) >> 5) + 1);
+      const int e = min(hh, X), s = max(l, 0);
+      cov_pos = cu + (e >= s ? e - s + 1 : 0);
     }
     ccnt = min<long long>(ccnt, P.max_chunks);
     // span edges: Lu per covered x >= 0 with x <= 64u, and max(0, Lu + x)
@@ -226,19 +305,36 @@ __global__ __launch_bounds__(256) void vs_cols_kernel(TileParams P) {
     const int32_t* cols = P.vert_idx + (size_t)bh * P.max_v;
     int32_t* out = P.t.cols + bu * P.max_v;
     int cnt = 0;
-    for (int base = 0; base < nv; base += 64) {
-      const int k = base + lane;
-      const int c = k < nv ? cols[k] : 0x7fffffff;
-      const bool in_range = c <= row_end;
-      const bool keep = in_range && !covered(bm, row0 - c);
-      const unsigned long long m = __ballot(keep);
-      const int pos = cnt + __popcll(m & ((1ull << lane) - 1ull));
-      if (keep) {
-        out[pos] = c;
-        edges += row_end - max(c, row0) + 1;
+    bool done = false;
+    for (int base = 0; base < nv && !done; base += 256) {
+      int c[4];
+      uint32_t wd[4];
+      #pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int k = base + 64 * j + lane;
+        c[j] = k < nv ? cols[k] : 0x7fffffff;
       }
-      cnt += __popcll(m);
-      if (__any(!in_range)) break;   // columns are ascending: the rest lie beyond the block
+      #pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        // x = row0 - c lies in [-63, n) for an in-range column
+        const int i = row0 - c[j] + 63;
+        wd[j] = c[j] <= row_end ? bm[i >> 5] : 0xffffffffu;
+      }
+      #pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        if (done) break;
+        const bool in_range = c[j] <= row_end;
+        const int i = row0 - c[j] + 63;
+        const bool keep = in_range && !((wd[j] >> (i & 31)) & 1u);
+        const unsigned long long m = __ballot(keep);
+        const int pos = cnt + __popcll(m & ((1ull << lane) - 1ull));
+        if (keep) {
+          out[pos] = c[j];
+          edges += row_end - max(c[j], row0) + 1;
+        }
+        cnt += __popcll(m);
+        if (__any(!in_range)) done = true;   // columns are ascending: the rest lie beyond the block
+      }
     }
     if (lane == 0) P.t.col_cnt[bu] = cnt;
     if (P.slash_tile == 1) edges = 0;   // exact slash pairs: counted by vs_exact_edges_kernel
@@ -319,12 +415,14 @@ __global__ __launch_bounds__(256) void vs_exact_edges_kernel(TileParams P) {
   }
 }
 
-// 4) Block-Sparse: validate J_u and count the kept block areas.
+// 4) Block-Sparse: validate J_u and count the kept block areas.  One wave
+//    per query block, 64 entries of J_u per round.
 __global__ __launch_bounds__(256) void bs_edges_kernel(TileParams P) {
   const int bh = blockIdx.y;
   const int h = bh % P.Hq;
   if (P.ht.kind[h] != MINF_BSPARSE) return;
-  const int u = blockIdx.x * 256 + threadIdx.x;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int u = blockIdx.x * 4 + wave;
   __shared__ unsigned long long part[4];
   unsigned long long edges = 0;
   if (u < P.nq) {
@@ -333,17 +431,20 @@ __global__ __launch_bounds__(256) void bs_edges_kernel(TileParams P) {
     const int Lu = min(64, P.n - 64 * u);
     bool bad = cnt < 0 || cnt > P.max_kb || cnt > u + 1;
     const int32_t* J = P.blk_idx + bu * P.max_kb;
-    int prev = -1;
-    for (int i = 0; !bad && i < cnt; ++i) {
-      const int v = J[i];
-      if (v <= prev || v > u) { bad = true; break; }
-      edges += (v < u) ? (unsigned long long)Lu * 64ull : (unsigned long long)(Lu * (Lu + 1) / 2);
-      prev = v;
+    for (int base = 0; !bad && base < cnt; base += 64) {
+      const int i = base + lane;
+      const int v = i < cnt ? J[i] : 0;
+      const int prev = (i < cnt && i > 0) ? J[i - 1] : -1;
+      if (__any(i < cnt && (v <= prev || v > u))) bad = true;
+      if (i < cnt) edges += (v < u) ? (unsigned long long)Lu * 64ull : (unsigned long long)(Lu * (Lu + 1) / 2);
     }
-    if (bad) { atomicOr(P.t.status, MINF_DEV_BAD_BLOCK); edges = 0; }
+    if (bad) {
+      if (lane == 0) atomicOr(P.t.status, MINF_DEV_BAD_BLOCK);
+      edges = 0;
+    }
   }
   for (int off = 32; off > 0; off >>= 1) edges += __shfl_xor(edges, off);
-  if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = edges;
+  if (lane == 0) part[wave] = edges;
   __syncthreads();
   if (threadIdx.x == 0) {
     const unsigned long long tot = part[0] + part[1] + part[2] + part[3];
@@ -362,7 +463,7 @@ hipError_t launch_tiles(const TileParams& p, bool has_vs, bool has_bs, hipStream
       hipLaunchKernelGGL(vs_exact_edges_kernel, dim3(BH), dim3(256), 0, st, p);
     }
   }
-  if (has_bs) hipLaunchKernelGGL(bs_edges_kernel, dim3((p.nq + 255) / 256, BH), dim3(256), 0, st, p);
+  if (has_bs) hipLaunchKernelGGL(bs_edges_kernel, dim3((p.nq + 3) / 4, BH), dim3(256), 0, st, p);
   return hipGetLastError();
 }
 
