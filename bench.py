@@ -83,7 +83,8 @@ def attn_traffic(workload):
 def computed_pairs(p, t, buf):
     """(query row, key) pairs the attention kernel computes: 64 x 32 per
     chunk of every query block (sink and window chunks, slash-span chunks,
-    gathered-column chunks, two chunks per selected block).  kept / computed
+    packed chunks of span tails, gathered-column chunks, two chunks per
+    selected block).  kept / computed
     is the tile efficiency E_h / E~_h."""
     import numpy as np
     from synth import gen
@@ -91,12 +92,14 @@ def computed_pairs(p, t, buf):
     u = np.arange(nq, dtype=np.int64)
     total = 0
     cc = t["chunk_cnt"].cpu().numpy() if "chunk_cnt" in t else None
+    pk = t["pk_cnt"].cpu().numpy() if "pk_cnt" in t else None
     colc = t["col_cnt"].cpu().numpy() if "col_cnt" in t else None
     bc = buf["blk_cnt"].cpu().numpy()
     for b in range(p.B):
         for h, c in enumerate(p.heads):
             if c.kind == gen.VSLASH:
-                chunks = cc[b, h].astype(np.int64) + (colc[b, h].astype(np.int64) + 31) // 32
+                chunks = (cc[b, h].astype(np.int64) + pk[b, h].astype(np.int64) +
+                          (colc[b, h].astype(np.int64) + 31) // 32)
             elif c.kind == gen.BSPARSE:
                 chunks = 2 * bc[b, h].astype(np.int64)
             else:

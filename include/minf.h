@@ -63,6 +63,13 @@ typedef enum { MINF_ASHAPE = 0, MINF_VSLASH = 1, MINF_BSPARSE = 2 } minf_kind;
 
 enum { MINF_FORCE_FIRST_BLOCK = 1, MINF_FORCE_DIAG_BLOCK = 2 };
 enum { MINF_MAX_HEADS = 64, MINF_BLOCK = 64, MINF_MAX_LAST_Q = 64, MINF_CHUNK = 32 };
+/* Offset that pads the tail list of minf_tiles: 64u - MINF_TAIL_PAD is
+ * negative for every block, so a padding entry covers no key.  Span tails
+ * are packed only for sequences of at most MINF_PACK_MAX_N tokens (measured:
+ * faster at 32K and 128K; slower at 1M, where the attention is bound by
+ * memory traffic and packed chunks gather scattered rows); longer sequences
+ * keep every range's tail as a chunk of its own and an empty tail list. */
+enum { MINF_TAIL_PAD = 1 << 30, MINF_PACK_MAX_N = 1 << 18 };
 
 /* One query head's entry in the layer's pattern table (MInference page,
  * section 6.3: pattern kind, vertical count, slash count, block count,
@@ -110,6 +117,8 @@ typedef struct {
   int64_t ws_bytes;    /* workspace bytes that suffice for every call below          */
   int64_t bits_words;  /* 32-bit words of each per-head bitmap of minf_tiles when
                           slash_tile == 1 and the layer has a VS head, else 0      */
+  int64_t max_tail;    /* entries of each per-head tail list of minf_tiles (a
+                          multiple of 32)                                          */
 } minf_sizes;
 
 /* Tile lists produced by minf_build_tiles and read by minf_sparse_attn.
@@ -120,12 +129,27 @@ typedef struct {
  *                     is slash-covered iff 64u - j lies in one of them, so one
  *                     list serves every query block.
  *   span_cnt          [B, Hq]             number of ranges.
- *   chunk_lo, chunk_hi [B, Hq, max_chunks] every range cut into pieces of at
- *                     most 32 offsets (chunk_hi - chunk_lo <= 31), ascending.
- *                     For block u a chunk covers the contiguous keys
- *                     [64u - chunk_hi, 64u - chunk_lo].
+ *   chunk_lo, chunk_hi [B, Hq, max_chunks] the whole 32-offset pieces of the
+ *                     ranges, each range cut from its low end
+ *                     (chunk_hi - chunk_lo = 31), ascending.  For block u a
+ *                     chunk covers the 32 contiguous keys
+ *                     [64u - chunk_hi, 64u - chunk_lo].  Under slash_tile == 1
+ *                     or for n > MINF_PACK_MAX_N a range's last, shorter piece
+ *                     is listed here too (chunk_hi - chunk_lo <= 31) and the
+ *                     tail list is empty.
  *   chunk_cnt         [B, Hq, nq]         chunks of block u: those whose
  *                     chunk_lo <= 64u (the others lie before key 0).
+ *   tail_x            [B, Hq, max_tail]   the offsets x of every range's last
+ *                     piece shorter than 32, all ranges together, ascending;
+ *                     entries from tail_cnt up to the next multiple of 32 hold
+ *                     MINF_TAIL_PAD (they cover no key).  Entries 32c ..
+ *                     32c+31 form packed chunk c: for block u its keys are
+ *                     64u - x (the same for every row of the block), so the
+ *                     list, like the chunk list, serves every query block.
+ *   tail_cnt          [B, Hq]             entries of tail_x in use (before
+ *                     the padding).
+ *   pk_cnt            [B, Hq, nq]         packed chunks of block u: those
+ *                     whose first entry tail_x[32c] <= 64u.
  *   cols              [B, Hq, nq, max_v]  for block u, the selected vertical
  *                     columns j <= min(64u+63, n-1) NOT covered by a slash
  *                     span of block u, ascending (MInference page section 4.1:
@@ -155,6 +179,9 @@ typedef struct {
   int32_t* status;
   uint32_t* slash_bits;
   uint32_t* col_bits;
+  int32_t* tail_x;
+  int32_t* tail_cnt;
+  int32_t* pk_cnt;
 } minf_tiles;
 
 enum {

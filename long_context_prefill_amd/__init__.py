@@ -36,6 +36,7 @@ MINF_ASHAPE, MINF_VSLASH, MINF_BSPARSE = 0, 1, 2
 MINF_FORCE_FIRST_BLOCK, MINF_FORCE_DIAG_BLOCK = 1, 2
 MINF_DEV_BAD_VERTICAL, MINF_DEV_BAD_SLASH, MINF_DEV_BAD_BLOCK, MINF_DEV_CAPACITY = 1, 2, 4, 8
 MINF_DEV_WAIT_EXHAUSTED = 16
+MINF_TAIL_PAD, MINF_PACK_MAX_N = 1 << 30, 1 << 18
 
 EXPORTED = ["minf_query_sizes", "minf_vs_index", "minf_vs_index_fused", "minf_bs_index", "minf_build_tiles",
             "minf_sparse_attn", "minf_sparse_attn_static", "minf_output_error", "minf_captured_mass", "minf_ragged_ws_bytes",
@@ -65,13 +66,14 @@ class MinfHeadCfg(ctypes.Structure):
 class MinfSizes(ctypes.Structure):
     _fields_ = [("nq", ctypes.c_int64), ("max_v", ctypes.c_int64), ("max_s", ctypes.c_int64),
                 ("max_kb", ctypes.c_int64), ("max_chunks", ctypes.c_int64), ("ws_bytes", ctypes.c_int64),
-                ("bits_words", ctypes.c_int64)]
+                ("bits_words", ctypes.c_int64), ("max_tail", ctypes.c_int64)]
 
 
 class MinfTiles(ctypes.Structure):
     _fields_ = [(name, ctypes.c_void_p) for name in
                 ("span_lo", "span_hi", "span_cnt", "chunk_lo", "chunk_hi", "chunk_cnt",
-                 "cols", "col_cnt", "kept_edges", "status", "slash_bits", "col_bits")]
+                 "cols", "col_cnt", "kept_edges", "status", "slash_bits", "col_bits", "tail_x", "tail_cnt",
+                 "pk_cnt")]
 
 
 _lib = None
@@ -299,6 +301,9 @@ def alloc_buffers(prob: MinfProblem, heads, device="cuda"):
             "chunk_cnt": torch.zeros((B, Hq, nq), **i32),
             "cols": torch.zeros((B, Hq, nq, int(sz.max_v) or 1), **i32),
             "col_cnt": torch.zeros((B, Hq, nq), **i32),
+            "tail_x": torch.zeros((B, Hq, int(sz.max_tail)), **i32),
+            "tail_cnt": torch.zeros((B, Hq), **i32),
+            "pk_cnt": torch.zeros((B, Hq, nq), **i32),
             "kept_edges": torch.zeros((B, Hq), dtype=torch.int64, device=device),
             "status": torch.zeros(1, **i32),
         },

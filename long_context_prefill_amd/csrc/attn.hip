@@ -51,6 +51,8 @@ struct ChunkDesc {
   int vlo, vhi;          // valid keys (contiguous chunks)
   const int32_t* gp;     // key list (gathered chunks) or nullptr
   int gcnt;              // valid entries of gp
+  int gbase;             // gathered keys: gbase - entry (span tails, entries are offsets) when gneg
+  bool gneg;
   int win;               // > 0: window lower bound j >= i - win + 1 applies
   bool mask;             // per-element test needed
   bool exact;            // a slash span chunk under exact pairs (slash_tile == 1)
@@ -199,12 +201,13 @@ __global__ __launch_bounds__(256, 1) void attn_kernel(AttnParams P) {
   const T* sq = reinterpret_cast<const T*>(smem);
 
   // ---- chunk counts of this item
-  int Ca = 0, Cb = 0;
+  int Ca = 0, Cb = 0, Cf = 0;
   int sink_len = 0, wlo = 0, whi = -1, win = 0, ncols = 0;
   const int32_t* colrow = nullptr;
   const int32_t* blkrow = nullptr;
   const int32_t* clo = nullptr;
   const int32_t* chi = nullptr;
+  const int32_t* tx = nullptr;
   if (kind == MINF_ASHAPE) {
     const int gk = P.ht.a[h];
     win = P.ht.b[h];
@@ -217,7 +220,10 @@ __global__ __launch_bounds__(256, 1) void attn_kernel(AttnParams P) {
     }
   } else if (kind == MINF_VSLASH) {
     // counts are clamped to the capacities so that no list is read past its end
-    Ca = min((long long)max(SV.chunk_cnt[hu], 0), (long long)SV.max_chunks);
+    // whole span chunks, then packed chunks of span tails
+    Cf = min((long long)max(SV.chunk_cnt[hu], 0), (long long)SV.max_chunks);
+    Ca = Cf + min((long long)max(SV.pk_cnt[hu], 0), (long long)(SV.max_tail >> 5));
+    tx = SV.tail_x + (int64_t)h * SV.max_tail;
     ncols = min((long long)max(SV.col_cnt[hu], 0), (long long)SV.max_v);
     Cb = (ncols + 31) >> 5;
     colrow = SV.cols + hu * SV.max_v;
@@ -230,6 +236,7 @@ __global__ __launch_bounds__(256, 1) void attn_kernel(AttnParams P) {
   // all of these are wave-uniform; keep them in scalar registers
   Ca = __builtin_amdgcn_readfirstlane(Ca);
   Cb = __builtin_amdgcn_readfirstlane(Cb);
+  Cf = __builtin_amdgcn_readfirstlane(Cf);
   sink_len = __builtin_amdgcn_readfirstlane(sink_len);
   wlo = __builtin_amdgcn_readfirstlane(wlo);
   whi = __builtin_amdgcn_readfirstlane(whi);
@@ -248,7 +255,7 @@ __global__ __launch_bounds__(256, 1) void attn_kernel(AttnParams P) {
 
   // ---- chunk description (wave-uniform)
   auto describe = [&](int k, ChunkDesc& d) {
-    d.gp = nullptr; d.gcnt = 0; d.win = 0; d.exact = false;
+    d.gp = nullptr; d.gcnt = 0; d.gbase = 0; d.gneg = false; d.win = 0; d.exact = false;
     if (kind == MINF_ASHAPE) {
       if (k < Ca) {
         d.kstart = 32 * k; d.vlo = 0; d.vhi = sink_len - 1;
@@ -256,10 +263,14 @@ __global__ __launch_bounds__(256, 1) void attn_kernel(AttnParams P) {
         d.kstart = wlo + 32 * (k - Ca); d.vlo = wlo; d.vhi = whi; d.win = win;
       }
     } else if (kind == MINF_VSLASH) {
-      if (k < Ca) {
+      if (k < Cf) {
         const int lo = clo[k], hi = chi[k];
         d.kstart = row0 - hi; d.vlo = max(0, d.kstart); d.vhi = min(row0 - lo, n - 1);
         d.exact = P.slash_tile == 1;
+      } else if (k < Ca) {
+        // 32 listed tail offsets x: keys 64u - x (padding entries fall below 0)
+        d.gp = tx + 32 * (k - Cf); d.gcnt = 32; d.gneg = true; d.gbase = row0;
+        d.kstart = 0; d.vlo = 0; d.vhi = n - 1;
       } else {
         const int kk = k - Ca;
         d.gp = colrow + 32 * kk; d.gcnt = min(32, ncols - 32 * kk);
@@ -291,7 +302,7 @@ __global__ __launch_bounds__(256, 1) void attn_kernel(AttnParams P) {
       int key;
       if (d.gp) {
         key = d.gp[p];                 // lists are padded to a multiple of 32 entries
-        key = p < d.gcnt ? key : 0;
+        key = p < d.gcnt ? (d.gneg ? d.gbase - key : key) : 0;
       } else {
         key = d.kstart + p;
       }
@@ -303,6 +314,7 @@ __global__ __launch_bounds__(256, 1) void attn_kernel(AttnParams P) {
       int key;
       if (d.gp) {
         key = d.gp[p];
+        if (d.gneg) key = d.gbase - key;
         key = (p < d.gcnt && key >= 0 && key < n) ? key : -1;
       } else {
         key = d.kstart + p;
@@ -429,12 +441,12 @@ __global__ __launch_bounds__(256, 1) void attn_kernel(AttnParams P) {
 
   // Contiguous chunks are loaded from a wave-uniform base (the chunk's first
   // key, clamped so that all 32 rows lie inside [0, n)) plus constant per-lane
-  // offsets; gathered chunks (vertical columns) and tiny sequences use
-  // per-lane key indices.
+  // offsets; gathered chunks (packed span tails, vertical columns) and tiny
+  // sequences use per-lane key indices.
   int vpos_c[8];
   #pragma unroll
   for (int e = 0; e < 8; ++e) vpos_c[e] = vpos(g, e);
-  const int Cfast = (n < 32) ? 0 : (kind == MINF_VSLASH ? Ca : C);
+  const int Cfast = (n < 32) ? 0 : (kind == MINF_VSLASH ? Cf : C);
   auto load_base = [&](const ChunkDesc& d) { return min(max(d.kstart, 0), n - 32); };
   auto fast_load_k = [&](int lb, typename O::KOp (&kop)[2][KS]) {
     const T* Kc = Kb + (size_t)lb * DH;

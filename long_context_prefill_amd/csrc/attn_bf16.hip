@@ -53,12 +53,15 @@ typedef short short4_t __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) short4_t lds_short4;
 typedef __attribute__((address_space(3))) const u32x4 lds_u32x4;
 typedef __attribute__((address_space(3))) char lds_char;
+typedef __attribute__((address_space(3))) const int32_t lds_i32;
 
 constexpr int kDH = 128;
 constexpr int kRowB = kDH * 2;          // bytes per K or V row
 constexpr int kTileB = 32 * kRowB;      // 8 KiB: one chunk of K (or V)
 constexpr int kSlotB = 2 * kTileB;      // K then V
-constexpr int kSmem = 2 * kSlotB;       // two slots
+constexpr int kRing = 2 * kSlotB;       // two K/V slots
+constexpr int kListB = 32 * 4;          // one gathered chunk's 32 list entries
+constexpr int kSmem = kRing + 3 * kListB;   // plus a ring of three entry lists
 constexpr float kTau = 8.0f;
 constexpr float kMInit = -1.0e30f;      // running maximum before any key (finite)
 
@@ -86,6 +89,7 @@ constexpr int kNone = 4;     // no pair of this wave's rows is kept
 constexpr int kGather = 8;   // keys are column-list entries kstart .. kstart+vhi-1
 constexpr int kWin = 16;     // an A-shape window chunk: keys j >= i - window + 1 only
 constexpr int kExact = 32;   // a slash span chunk under exact pairs (slash_tile == 1)
+constexpr int kNeg = 64;     // gathered from the tail list: entries are offsets x, keys 64u - x
 struct Chunk {
   int kstart;   // first key (contiguous) or first column-list entry (gathered)
   int vlo, vhi; // contiguous: keys kept within the chunk; gathered: vhi = entries
@@ -94,18 +98,21 @@ struct Chunk {
 
 // The chunk lists of one work item (head h of sequence S, query block u): Ca chunks
 // of the first list (sink, slash spans or selected blocks) and Cb of the
-// second (window or gathered columns).  Shared by the cost pass of the
+// second (window or gathered columns).  For Vertical-Slash heads the first
+// list is Cf whole 32-offset span chunks followed by Ca - Cf packed chunks of
+// span tails (32 listed offsets x each, keys 64u - x).  Shared by the cost pass of the
 // scheduler and the attention kernel.
 struct ItemLists {
-  int Ca, Cb, sink_len, wlo, whi, win, ncols;
+  int Ca, Cb, Cf, sink_len, wlo, whi, win, ncols;
   const int32_t* colrow;
+  const int32_t* tx;
   const int32_t* blkrow;
   const int32_t* clo;
   const int32_t* chi;
 };
 
 __device__ __forceinline__ ItemLists item_lists(const AttnParams& P, const SampleView& S, int h, int kind, int u) {
-  ItemLists L{0, 0, 0, 0, -1, 0, 0, nullptr, nullptr, nullptr, nullptr};
+  ItemLists L{0, 0, 0, 0, 0, -1, 0, 0, nullptr, nullptr, nullptr, nullptr, nullptr};
   const int n = S.n, row0 = 64 * u;
   const int64_t hu = (int64_t)h * S.nq + u;
   if (kind == MINF_ASHAPE) {
@@ -120,7 +127,12 @@ __device__ __forceinline__ ItemLists item_lists(const AttnParams& P, const Sampl
     }
   } else if (kind == MINF_VSLASH) {
     // counts are clamped to the capacities so that no list is read past its end
-    L.Ca = (int)min((long long)max(ld_uniform(S.chunk_cnt, hu), 0), (long long)S.max_chunks);
+    L.Cf = (int)min((long long)max(ld_uniform(S.chunk_cnt, hu), 0), (long long)S.max_chunks);
+    L.Ca = L.Cf + (int)min((long long)max(ld_uniform(S.pk_cnt, hu), 0), (long long)(S.max_tail >> 5));
+    // (the stride passes through readfirstlane: without it the compiler
+    // kept the tail list's base in vector registers and failed to build the
+    // scalar loads of its entries)
+    L.tx = S.tail_x + (int64_t)h * __builtin_amdgcn_readfirstlane((int)S.max_tail);
     L.ncols = (int)min((long long)max(ld_uniform(S.col_cnt, hu), 0), (long long)S.max_v);
     L.Cb = (L.ncols + 31) >> 5;
     L.colrow = S.cols + hu * S.max_v;
@@ -364,6 +376,19 @@ __device__ __forceinline__ void copy_rows(const char* base, const uint32_t (&vof
       : "memory", "scc", "m0");
 }
 
+// The 32 list entries of a gathered chunk (4 bytes per lane, lanes 0..31)
+// into LDS at dst, as one more direct global->LDS copy: it completes with the
+// chunk copies, before the barrier that ends the iteration.
+__device__ __forceinline__ void copy_entries(const int32_t* base, uint32_t voff, uint32_t dst) {
+  asm volatile(
+      "s_mov_b32 m0, %2\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dword %0, %1"
+      :
+      : "v"(voff), "s"(base), "s"(dst)
+      : "memory", "m0");
+}
+
 // This wave's copies have landed and its LDS reads have returned; after the
 // barrier the same holds for the other wave, so both may read what was copied
 // and rewrite what was read.
@@ -404,6 +429,7 @@ __device__ __forceinline__ void attn_item(const AttnParams& P, const SampleView&
   const ItemLists L = item_lists(P, S, h, KIND, u);
   const int Ca = __builtin_amdgcn_readfirstlane(L.Ca);
   const int Cb = __builtin_amdgcn_readfirstlane(L.Cb);
+  const int Cf = __builtin_amdgcn_readfirstlane(L.Cf);
   const int C = Ca + Cb;
   if (C <= 0) {
     // nothing kept: o = 0, lse = -inf
@@ -455,11 +481,21 @@ __device__ __forceinline__ void attn_item(const AttnParams& P, const SampleView&
   auto fetch = [&](int k) {
     Raw r{0, 0};
     if constexpr (KIND == MINF_VSLASH) {
-      const bool span = k < Ca;
-      const int e = 32 * (k - Ca);
-      const int cnt = min(32, ncols - e);
-      r.a = ld_uniform(span ? L.clo : L.colrow, span ? k : e);
-      r.b = ld_uniform(span ? L.chi : L.colrow, span ? k : e + cnt - 1);
+      // span chunk: its two offsets; packed tail chunk: its first and last
+      // offset; gathered columns: the first and last column
+      if (k < Cf) {
+        r.a = ld_uniform(L.clo, k);
+        r.b = ld_uniform(L.chi, k);
+      } else if (k < Ca) {
+        const int e = 32 * (k - Cf);
+        r.a = ld_uniform(L.tx, e);
+        r.b = ld_uniform(L.tx, e + 31);
+      } else {
+        const int e = 32 * (k - Ca);
+        const int cnt = min(32, ncols - e);
+        r.a = ld_uniform(L.colrow, e);
+        r.b = ld_uniform(L.colrow, e + cnt - 1);
+      }
     } else if constexpr (KIND == MINF_BSPARSE) {
       r.a = ld_uniform(L.blkrow, k >> 1);
     }
@@ -474,18 +510,27 @@ __device__ __forceinline__ void attn_item(const AttnParams& P, const SampleView&
       d.vhi = min(d.kstart + 31, w ? whi : sink_len - 1);
       d.flags = cflags(d.kstart, d.vlo, d.vhi, w) | (w ? kWin : 0);
     } else if constexpr (KIND == MINF_VSLASH) {
-      if (k < Ca) {
+      if (k < Cf) {
         const int lo = r.a, hi = r.b;
         d.kstart = row0 - hi;
         d.vlo = max(0, d.kstart);
         d.vhi = min(row0 - lo, n - 1);
         d.flags = cflags(d.kstart, d.vlo, d.vhi, false);
         if (exact && !(d.flags & kNone)) d.flags |= kMask | kExact;
+      } else if (k < Ca) {
+        // packed tail chunk: keys 64u - x for its 32 ascending offsets x
+        // (padding offsets give negative keys); the largest key comes from
+        // the first offset, the smallest from the last
+        const int kmax = row0 - r.a, kmin = row0 - r.b;
+        d.kstart = k % 3;   // the LDS slot of its entries
+        d.vlo = 0;
+        d.vhi = 32;
+        d.flags = kGather | kNeg | ((kmax < 0 || kmin > rlast) ? kNone : 0) | ((kmin < 0 || kmax > rw0) ? kMask : 0);
       } else {
         const int e = 32 * (k - Ca);
         const int cnt = min(32, ncols - e);
         const int gfirst = r.a, glast = r.b;
-        d.kstart = e;
+        d.kstart = k % 3;   // the LDS slot of its entries
         d.vlo = 0;
         d.vhi = cnt;
         d.flags = kGather | (gfirst > rlast ? kNone : 0) | ((cnt < 32 || glast > rw0) ? kMask : 0);
@@ -525,7 +570,7 @@ __device__ __forceinline__ void attn_item(const AttnParams& P, const SampleView&
       if (r.a >= 0 && r.a < u) return Chunk{64 * r.a + 32 * (k & 1), 0, 0, kFast};
     } else {
       const int ks = row0 - r.b;
-      if (k < Ca && !exact && r.b - r.a == 31 && ks >= 0 && r.b >= hmin && ks <= n - 32)
+      if (k < Cf && !exact && r.b - r.a == 31 && ks >= 0 && r.b >= hmin && ks <= n - 32)
         return Chunk{ks, 0, 0, kFast};
     }
     return decode(k, r);
@@ -546,6 +591,18 @@ __device__ __forceinline__ void attn_item(const AttnParams& P, const SampleView&
     voff[i] = (uint32_t)(r * kRowB + 16 * (cpiece ^ (4 * (r & 3))) - 1024 * i);
   }
   const uint32_t lds_base = (uint32_t)(uintptr_t)smem + 4096 * wave;
+  // the entry ring: gathered chunk k keeps its 32 list entries in slot k % 3
+  // from two iterations before its K copy until the iteration of its V copy
+  const uint32_t lst_base = (uint32_t)(uintptr_t)smem + kRing;
+  auto copy_list = [&](int k) {
+    if constexpr (KIND == MINF_VSLASH) {
+      if (k >= Cf && wave == 0) {
+        const int32_t* src = k < Ca ? L.tx + 32 * (k - Cf) : L.colrow + 32 * (k - Ca);
+        const uint32_t dst = __builtin_amdgcn_readfirstlane(lst_base + kListB * (k % 3));
+        if (lane < 32) copy_entries(src, 4 * lane, dst);
+      }
+    }
+  };
   // K rows (V rows) of chunk d into the K (V) half of slot sl
   auto issue = [&](const Chunk& d, int sl, bool is_v) {
     const char* src = is_v ? Vb : Kb;
@@ -554,17 +611,20 @@ __device__ __forceinline__ void attn_item(const AttnParams& P, const SampleView&
       copy_chunk(src + (size_t)d.kstart * kRowB, is_v ? voff : koff, dst);
     } else {
       // per-lane rows: clamped into [0, n) (the excess keys are masked) or
-      // gathered from the column list; all keys are read before any copy.
-      // (ks passes through an empty asm statement so that the per-lane
-      // arithmetic is not hoisted above the branch onto the fast path)
+      // gathered: the chunk's list entries were copied into the LDS entry
+      // ring two iterations earlier (columns are keys, tail offsets x give
+      // keys 64u - x).  (ks passes through an empty asm statement so that the
+      // per-lane arithmetic is not hoisted above the branch onto the fast path)
       int ks = d.kstart;
       asm volatile("" : "+s"(ks));
+      const lds_i32* ent = (const lds_i32*)(uintptr_t)(lst_base + kListB * ks);
       uint32_t o[4];
       #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int r = crow0 + 4 * i;
         int key = ks + r;
-        if (d.flags & kGather) key = r < d.vhi ? L.colrow[ks + r] : 0;
+        if (d.flags & kNeg) key = row0 - ent[r];
+        else if (d.flags & kGather) key = r < d.vhi ? ent[r] : 0;
         const uint32_t rb = (uint32_t)min(max(key, 0), n - 1) * kRowB;
         o[i] = rb + 16 * (cpiece ^ (is_v ? 4 * (r & 3) : (r & 15)));
       }
@@ -575,19 +635,22 @@ __device__ __forceinline__ void attn_item(const AttnParams& P, const SampleView&
   // Keep-bits of a chunk for this lane's row: bit 8a + b (a, b = 0..3) set
   // when the key at chunk position 8a + 4hh + b, which element 4a + b of
   // the lane holds, is kept.  Only for chunks with kMask; gathered chunks
-  // read their keys with vector loads, so this runs while no copy is in
-  // flight.
+  // read their list entries from the LDS entry ring.
   auto keep_bits = [&](const Chunk& d) -> uint32_t {
     if (!(d.flags & kMask) || (d.flags & kNone)) return 0u;
     if (d.flags & kGather) {
+      // listed columns are keys; listed tail offsets x give keys 64u - x,
+      // which may be negative (kept iff 0 <= key <= row)
+      const bool neg = d.flags & kNeg;
+      const lds_i32* ent = (const lds_i32*)(uintptr_t)(lst_base + kListB * d.kstart);
       uint32_t bits = 0;
       #pragma unroll
       for (int i = 0; i < 16; ++i) {
         const int pos = 8 * (i >> 2) + 4 * hh + (i & 3);
-        const int key = pos < d.vhi ? L.colrow[d.kstart + pos] : n;
-        bits |= (key <= myrow ? 1u : 0u) << (8 * (i >> 2) + (i & 3));
+        const int e = pos < d.vhi ? ent[pos] : n;
+        const int key = neg ? row0 - e : e;
+        bits |= ((uint32_t)key <= (uint32_t)myrow ? 1u : 0u) << (8 * (i >> 2) + (i & 3));
       }
-      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
       return bits;
     }
     const int lo = ((d.flags & kWin) ? max(d.vlo, myrow - win + 1) : d.vlo) - d.kstart;
@@ -720,6 +783,12 @@ __device__ __forceinline__ void attn_item(const AttnParams& P, const SampleView&
   //      copies issued in iteration j are V of chunk j+1 and K of chunk j+2, so
   //      every slot half is rewritten only after both waves have passed the
   //      barrier that ends its last use.
+  // list entries of the first three chunks (a gathered chunk among the
+  // first two is read below, so those are waited for)
+  copy_list(0);
+  if (C > 1) copy_list(1);
+  if (C > 2) copy_list(2);
+  if (KIND == MINF_VSLASH && Cf < 2) wait_copies_and_barrier();
   Chunk d0 = describe(kc), d1{0, 1, 0, kNone}, d2{0, 1, 0, kNone};
   issue(d0, 0, false);
   issue(d0, 0, true);
@@ -760,7 +829,10 @@ __device__ __forceinline__ void attn_item(const AttnParams& P, const SampleView&
       if (more2) {
         advance();
         d2 = decode_fast(kc, rn);
-        if (STEADY || j + 3 < C) rn = fetch(next_of(kc));
+        if (STEADY || j + 3 < C) {
+          rn = fetch(next_of(kc));
+          copy_list(next_of(kc));
+        }
       }
     }
     uint32_t bits1 = 0u;

@@ -33,7 +33,7 @@ int64_t round_up(int64_t x, int64_t m) { return (x + m - 1) / m * m; }
 constexpr int64_t kBsMaxBlocks = 256 * 128;
 
 struct Derived {
-  int64_t nq = 0, max_v = 0, max_s = 0, max_kb = 0, max_chunks = 0, bm_words = 0, bits_words = 0;
+  int64_t nq = 0, max_v = 0, max_s = 0, max_kb = 0, max_chunks = 0, bm_words = 0, bits_words = 0, max_tail = 0;
   bool has_a = false, has_vs = false, has_bs = false;
   int hq_vs = 0, hq_bs = 0;
   minf::HeadTable ht{};
@@ -107,6 +107,9 @@ minf_status validate(const minf_problem* p, const minf_head_cfg* heads, Derived*
   d->max_chunks = (p->n + 63 + 31) / 32 + d->max_s + 1;
   d->bm_words = (p->n + 63 + 31) / 32;
   d->bits_words = (p->slash_tile == 1 && d->has_vs) ? minf::exact_bits_words(p->n) : 0;
+  // every range leaves a tail of at most 31 offsets, and the tails are
+  // disjoint offsets in [-63, n); padded to whole packed chunks
+  d->max_tail = round_up(std::min<int64_t>(31 * d->max_s, (int64_t)p->n + 63), MINF_CHUNK);
   return MINF_OK;
 }
 
@@ -271,6 +274,7 @@ minf_status minf_query_sizes(const minf_problem* prob, const minf_head_cfg* head
   out->max_chunks = d.max_chunks;
   out->ws_bytes = (int64_t)ws_total(prob, d);
   out->bits_words = d.bits_words;
+  out->max_tail = d.max_tail;
   return MINF_OK;
 }
 
@@ -346,8 +350,9 @@ minf_status minf_build_tiles(const minf_problem* prob, const minf_head_cfg* head
   if (s != MINF_OK) return s;
   if (!tiles || !tiles->kept_edges || !tiles->status) return fail(MINF_EINVAL, "null tiles, kept_edges or status");
   if (d.has_vs && (!vert_idx || !slash_idx || !tiles->span_lo || !tiles->span_hi || !tiles->span_cnt ||
-                   !tiles->chunk_lo || !tiles->chunk_hi || !tiles->chunk_cnt || !tiles->cols || !tiles->col_cnt))
-    return fail(MINF_EINVAL, "a Vertical-Slash head needs vert_idx, slash_idx and every span/chunk/column buffer");
+                   !tiles->chunk_lo || !tiles->chunk_hi || !tiles->chunk_cnt || !tiles->cols || !tiles->col_cnt ||
+                   !tiles->tail_x || !tiles->tail_cnt || !tiles->pk_cnt))
+    return fail(MINF_EINVAL, "a Vertical-Slash head needs vert_idx, slash_idx and every span/chunk/tail/column buffer");
   if (d.has_bs && (!blk_idx || !blk_cnt)) return fail(MINF_EINVAL, "a Block-Sparse head needs blk_idx and blk_cnt");
   if (d.bits_words > 0 && (!tiles->slash_bits || !tiles->col_bits))
     return fail(MINF_EINVAL, "slash_tile=1 with a Vertical-Slash head needs slash_bits and col_bits");
@@ -362,6 +367,7 @@ minf_status minf_build_tiles(const minf_problem* prob, const minf_head_cfg* head
   t.bitmap = reinterpret_cast<uint32_t*>(base + w.bitmap);
   t.head_ok = reinterpret_cast<int32_t*>(base + w.head_ok);
   t.max_v = d.max_v; t.max_s = d.max_s; t.max_kb = d.max_kb; t.max_chunks = d.max_chunks; t.bm_words = d.bm_words;
+  t.max_tail = d.max_tail;
   t.bits_words = d.bits_words; t.slash_tile = prob->slash_tile;
   t.B = prob->B; t.Hq = prob->Hq; t.n = prob->n; t.nq = (int)d.nq;
   t.ht = d.ht;
@@ -377,7 +383,8 @@ static minf_status attn_checks(const minf_problem* prob, const minf_head_cfg* he
   if (s != MINF_OK) return s;
   if (!Q || !K || !V || !O) return fail(MINF_EINVAL, "null Q, K, V or O");
   if (d->has_bs && (!blk_idx || !blk_cnt)) return fail(MINF_EINVAL, "a Block-Sparse head needs blk_idx and blk_cnt");
-  if (d->has_vs && (!tiles || !tiles->chunk_lo || !tiles->chunk_hi || !tiles->chunk_cnt || !tiles->cols || !tiles->col_cnt))
+  if (d->has_vs && (!tiles || !tiles->chunk_lo || !tiles->chunk_hi || !tiles->chunk_cnt || !tiles->cols ||
+                    !tiles->col_cnt || !tiles->tail_x || !tiles->pk_cnt))
     return fail(MINF_EINVAL, "a Vertical-Slash head needs the tile lists from minf_build_tiles");
   if (d->bits_words > 0 && (!tiles->slash_bits || !tiles->col_bits))
     return fail(MINF_EINVAL, "slash_tile=1 with a Vertical-Slash head needs slash_bits and col_bits");
@@ -406,9 +413,10 @@ static minf_status attn_launch(const minf_problem* prob, const Derived& d, const
   if (d.has_vs && !samples) {
     a.chunk_lo = tiles->chunk_lo; a.chunk_hi = tiles->chunk_hi; a.chunk_cnt = tiles->chunk_cnt;
     a.cols = tiles->cols; a.col_cnt = tiles->col_cnt;
+    a.tail_x = tiles->tail_x; a.pk_cnt = tiles->pk_cnt;
   }
   a.samples = samples;
-  a.max_kb = d.max_kb; a.max_chunks = d.max_chunks; a.max_v = d.max_v;
+  a.max_kb = d.max_kb; a.max_chunks = d.max_chunks; a.max_v = d.max_v; a.max_tail = d.max_tail;
   a.B = prob->B; a.Hq = prob->Hq; a.Hkv = prob->Hkv; a.n = prob->n; a.nq = (int)d.nq;
   a.gsz = prob->Hq / prob->Hkv;
   a.n_utiles = (int)((d.nq + 7) / 8);
@@ -459,7 +467,7 @@ minf_status minf_sparse_attn_static(const minf_problem* prob, const minf_head_cf
 // descriptors that the one attention launch reads.
 struct RaggedRegion {
   size_t vert, slash, blk, blkcnt, span_lo, span_hi, span_cnt, chunk_lo, chunk_hi, chunk_cnt, cols, col_cnt, sbits,
-      cbits;
+      cbits, tail_x, tail_cnt, pk_cnt;
   Derived d;
 };
 struct RaggedLayout {
@@ -507,6 +515,9 @@ static minf_status ragged_layout(const minf_problem* prob, const minf_head_cfg* 
     R.col_cnt = c.take(4 * Hq * nq);
     R.sbits = c.take(4 * Hq * std::max<int64_t>(d.bits_words, 1));
     R.cbits = c.take(4 * Hq * std::max<int64_t>(d.bits_words, 1));
+    R.tail_x = c.take(4 * Hq * std::max<int64_t>(d.max_tail, 1));
+    R.tail_cnt = c.take(4 * Hq);
+    R.pk_cnt = c.take(4 * Hq * nq);
     stage = std::max(stage, ws_total(&one, d));
   }
   L->all = *prob;
@@ -598,6 +609,9 @@ minf_status minf_prefill_ragged(const minf_problem* prob, const minf_head_cfg* h
     t.col_cnt = reinterpret_cast<int32_t*>(w + R.col_cnt);
     t.slash_bits = reinterpret_cast<uint32_t*>(w + R.sbits);
     t.col_bits = reinterpret_cast<uint32_t*>(w + R.cbits);
+    t.tail_x = reinterpret_cast<int32_t*>(w + R.tail_x);
+    t.tail_cnt = reinterpret_cast<int32_t*>(w + R.tail_cnt);
+    t.pk_cnt = reinterpret_cast<int32_t*>(w + R.pk_cnt);
     t.status = status;
     // kept edges of this sample go straight to the caller's [B, Hq] array,
     // or to a scratch row of the workspace
@@ -622,7 +636,9 @@ minf_status minf_prefill_ragged(const minf_problem* prob, const minf_head_cfg* h
     D.blk_idx = blk; D.blk_cnt = blkcnt;
     D.slash_bits = R.d.bits_words > 0 ? t.slash_bits : nullptr;
     D.col_bits = R.d.bits_words > 0 ? t.col_bits : nullptr;
+    D.tail_x = t.tail_x; D.pk_cnt = t.pk_cnt;
     D.max_chunks = R.d.max_chunks; D.max_v = R.d.max_v; D.max_kb = R.d.max_kb; D.bits_words = R.d.bits_words;
+    D.max_tail = R.d.max_tail;
     D.n = seq_lens[b];
     D.nq = (int32_t)R.d.nq;
     if (in_batch == minf::kSampleBatch || b + 1 == prob->B) {

@@ -29,7 +29,9 @@ struct SampleDesc {
   const int32_t* blk_cnt;
   const uint32_t* slash_bits;
   const uint32_t* col_bits;
-  int64_t max_chunks, max_v, max_kb, bits_words;
+  const int32_t* tail_x;
+  const int32_t* pk_cnt;
+  int64_t max_chunks, max_v, max_kb, bits_words, max_tail;
   int32_t n, nq;
 };
 constexpr int kSampleBatch = 16;     // descriptors written per launch of the table writer
@@ -55,7 +57,9 @@ struct AttnParams {
   const int32_t* chunk_cnt;
   const int32_t* cols;
   const int32_t* col_cnt;
-  int64_t max_kb, max_chunks, max_v;
+  const int32_t* tail_x;     // [B,Hq,max_tail] packed tail offsets (minf_tiles.tail_x)
+  const int32_t* pk_cnt;     // [B,Hq,nq] packed chunks per block
+  int64_t max_kb, max_chunks, max_v, max_tail;
   int32_t B, Hq, Hkv, n, nq, gsz;
   int32_t n_utiles, n_segs;
   float c;          // scale * log2(e)
@@ -96,7 +100,9 @@ struct SampleView {
   const int32_t* blk_cnt;
   const uint32_t* slash_bits;
   const uint32_t* col_bits;
-  int64_t max_chunks, max_v, max_kb, bits_words;
+  const int32_t* tail_x;
+  const int32_t* pk_cnt;
+  int64_t max_chunks, max_v, max_kb, bits_words, max_tail;
 };
 __device__ __forceinline__ SampleView sample_view(const AttnParams& P, int b) {
   SampleView v;
@@ -107,7 +113,9 @@ __device__ __forceinline__ SampleView sample_view(const AttnParams& P, int b) {
     v.chunk_lo = d->chunk_lo; v.chunk_hi = d->chunk_hi; v.chunk_cnt = d->chunk_cnt;
     v.cols = d->cols; v.col_cnt = d->col_cnt; v.blk_idx = d->blk_idx; v.blk_cnt = d->blk_cnt;
     v.slash_bits = d->slash_bits; v.col_bits = d->col_bits;
+    v.tail_x = d->tail_x; v.pk_cnt = d->pk_cnt;
     v.max_chunks = d->max_chunks; v.max_v = d->max_v; v.max_kb = d->max_kb; v.bits_words = d->bits_words;
+    v.max_tail = d->max_tail;
   } else {
     const int64_t bq = (int64_t)b * P.Hq;
     v.n = P.n; v.nq = P.nq;
@@ -122,7 +130,10 @@ __device__ __forceinline__ SampleView sample_view(const AttnParams& P, int b) {
     v.blk_cnt = P.blk_cnt ? P.blk_cnt + bq * P.nq : nullptr;
     v.slash_bits = P.slash_bits ? P.slash_bits + bq * P.bits_words : nullptr;
     v.col_bits = P.col_bits ? P.col_bits + bq * P.bits_words : nullptr;
+    v.tail_x = P.tail_x ? P.tail_x + bq * P.max_tail : nullptr;
+    v.pk_cnt = P.pk_cnt ? P.pk_cnt + bq * P.nq : nullptr;
     v.max_chunks = P.max_chunks; v.max_v = P.max_v; v.max_kb = P.max_kb; v.bits_words = P.bits_words;
+    v.max_tail = P.max_tail;
   }
   return v;
 }
@@ -166,7 +177,7 @@ struct TileParams {
   int32_t* range_chunks;     // ws [B,Hq,max_s+1]: chunks before range r
   uint32_t* bitmap;          // ws [B,Hq,bm_words]: bit x+63 set iff x in S
   int32_t* head_ok;          // ws [B,Hq]
-  int64_t max_v, max_s, max_kb, max_chunks, bm_words;
+  int64_t max_v, max_s, max_kb, max_chunks, bm_words, max_tail;
   int64_t bits_words;        // words of t.slash_bits / t.col_bits (slash_tile == 1)
   int32_t slash_tile;
   int32_t B, Hq, n, nq;

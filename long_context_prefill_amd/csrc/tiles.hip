@@ -64,23 +64,24 @@ __device__ int block_exscan(int x, int* sh, int* total) {
 constexpr int kIPT = 8;
 constexpr int kRound = 256 * kIPT;
 
-// Last index r in [0, cnt) with a[r] <= x (a ascending), -1 if none, found
-// by one wave: up to 64 sampled entries per step, so a list of up to 4096
-// entries costs two rounds of loads instead of a dependent chain of twelve.
-__device__ __forceinline__ int wave_last_le(const int32_t* a, int cnt, int x) {
+// Last index r in [0, cnt) with a[r * step] <= x (ascending), -1 if none,
+// found by one wave: up to 64 sampled entries per round, so a list of up to
+// 4096 entries costs two rounds of loads instead of a dependent chain of
+// twelve.
+__device__ __forceinline__ int wave_last_le(const int32_t* a, int cnt, int x, int step = 1) {
   const int lane = threadIdx.x & 63;
   int lo = 0, hi = cnt;   // the answer lies in [lo - 1, hi - 1]; a[lo - 1] <= x when lo > 0
   while (hi - lo > 64) {
     const int stride = (hi - lo + 63) / 64;
     const int k = lo + lane * stride;
-    const int c = __popcll(__ballot(k < hi && a[k] <= x));   // sampled entries <= x form a prefix
+    const int c = __popcll(__ballot(k < hi && a[(int64_t)k * step] <= x));   // entries <= x form a prefix
     if (c == 0) { hi = lo; break; }
     const int nlo = lo + (c - 1) * stride;
     hi = min(hi, nlo + stride);
     lo = nlo;
   }
   const int k = lo + lane;
-  return lo - 1 + __popcll(__ballot(k < hi && a[k] <= x));
+  return lo - 1 + __popcll(__ballot(k < hi && a[(int64_t)k * step] <= x));
 }
 
 // 1) validate indices, initialise kept_edges, merge slash ranges.
@@ -166,8 +167,14 @@ __global__ __launch_bounds__(256) void vs_ranges_kernel(TileParams P) {
   if (threadIdx.x == 0) P.t.span_cnt[bh] = ok ? carry : 0;
 }
 
-// 2) cut ranges into chunks, prefix counts, coverage bitmap.  The bitmap is
-//    assembled in LDS, kSlabWords words at a time: a range is at least 64
+// 2) cut ranges into chunks, prefix counts, coverage bitmap.  Each range is
+//    cut into whole 32-offset chunks from its low end; the shorter last
+//    piece (its tail) goes to the per-head tail list, whose entries the
+//    attention packs 32 to a chunk (under exact slash pairs the tail stays a
+//    chunk of its own: the per-pair test needs contiguous keys; so it does
+//    beyond MINF_PACK_MAX_N tokens, where the walk's locality matters more
+//    than the partial chunks).  The bitmap
+//    is assembled in LDS, kSlabWords words at a time: a range is at least 64
 //    bits wide, so a word meets at most two ranges and every word is written
 //    once, whole.
 constexpr int kSlabWords = 8192;
@@ -177,6 +184,7 @@ __global__ __launch_bounds__(256) void vs_chunks_kernel(TileParams P) {
   const int bh = blockIdx.x;
   const int h = bh % P.Hq;
   if (P.ht.kind[h] != MINF_VSLASH) return;
+  const bool tails = P.slash_tile != 1 && P.n <= MINF_PACK_MAX_N;
   const int nr = P.t.span_cnt[bh];
   const int32_t* lo = P.t.span_lo + (size_t)bh * P.max_s;
   const int32_t* hi = P.t.span_hi + (size_t)bh * P.max_s;
@@ -184,7 +192,8 @@ __global__ __launch_bounds__(256) void vs_chunks_kernel(TileParams P) {
   int32_t* rch = P.range_chunks + (size_t)bh * (P.max_s + 1);
   int32_t* clo = P.t.chunk_lo + (size_t)bh * P.max_chunks;
   int32_t* chi = P.t.chunk_hi + (size_t)bh * P.max_chunks;
-  int carry_c = 0, carry_x = 0;
+  int32_t* tx = P.t.tail_x + (size_t)bh * P.max_tail;
+  int carry_c = 0, carry_x = 0, carry_t = 0;
   for (int base = 0; base < nr; base += kRound) {
     const int r0 = base + (int)threadIdx.x * kIPT;
     int a[kIPT], b[kIPT];
@@ -194,25 +203,26 @@ __global__ __launch_bounds__(256) void vs_chunks_kernel(TileParams P) {
       a[e] = r < nr ? lo[r] : 0;
       b[e] = r < nr ? hi[r] : -1;
     }
-    int sc = 0, sx = 0;
+    // chunks, covered offsets >= 0 and tail entries of each range
+    auto nchunks = [&](int e) { const int w = b[e] - a[e] + 1; return tails ? (w >> 5) : ((w + 31) >> 5); };
+    auto ntail = [&](int e) { return tails ? ((b[e] - a[e] + 1) & 31) : 0; };
+    auto ncov = [&](int e) { return b[e] >= 0 ? b[e] - max(a[e], 0) + 1 : 0; };
+    int sc = 0, sx = 0, st = 0;
     #pragma unroll
     for (int e = 0; e < kIPT; ++e) {
-      if (r0 + e < nr) {
-        sc += (b[e] - a[e] + 32) >> 5;
-        sx += b[e] >= 0 ? b[e] - max(a[e], 0) + 1 : 0;
-      }
+      if (r0 + e < nr) { sc += nchunks(e); sx += ncov(e); st += ntail(e); }
     }
-    int tc, tx;
+    int tc, tx_, tt;
     int pc = carry_c + block_exscan(sc, sh, &tc);
-    int px = carry_x + block_exscan(sx, sh, &tx);
+    int px = carry_x + block_exscan(sx, sh, &tx_);
+    int pt = carry_t + block_exscan(st, sh, &tt);
     #pragma unroll
     for (int e = 0; e < kIPT; ++e) {
       const int r = r0 + e;
       if (r < nr) {
         rch[r] = pc;
         cum[r] = px;
-        // the range's chunks of at most 32 offsets, from its low end
-        const int nch = (b[e] - a[e] + 32) >> 5;
+        const int nch = nchunks(e), nt = ntail(e);
         for (int m = 0; m < nch; ++m) {
           const int c = pc + m;
           if (c < P.max_chunks) {
@@ -220,12 +230,24 @@ __global__ __launch_bounds__(256) void vs_chunks_kernel(TileParams P) {
             chi[c] = min(a[e] + 32 * m + 31, b[e]);
           }
         }
+        for (int i = 0; i < nt; ++i)
+          if (pt + i < P.max_tail) tx[pt + i] = a[e] + 32 * nch + i;
         pc += nch;
-        px += b[e] >= 0 ? b[e] - max(a[e], 0) + 1 : 0;
+        px += ncov(e);
+        pt += nt;
       }
     }
     carry_c += tc;
-    carry_x += tx;
+    carry_x += tx_;
+    carry_t += tt;
+  }
+  // pad the tail list to whole packed chunks
+  const int tpad = (carry_t + 31) & ~31;
+  for (int i = carry_t + (int)threadIdx.x; i < tpad; i += 256)
+    if (i < P.max_tail) tx[i] = MINF_TAIL_PAD;
+  if (threadIdx.x == 0) {
+    P.t.tail_cnt[bh] = (int)min<long long>(carry_t, P.max_tail);
+    if (tpad > P.max_tail) atomicOr(P.t.status, MINF_DEV_CAPACITY);
   }
   if (threadIdx.x == 0) { rch[nr] = carry_c; cum[nr] = carry_x; }
   if (threadIdx.x == 0 && carry_c > P.max_chunks) atomicOr(P.t.status, MINF_DEV_CAPACITY);
@@ -285,16 +307,23 @@ __global__ __launch_bounds__(256) void vs_cols_kernel(TileParams P) {
     long long cov_pos = 0;  // |S intersect [0, X]|
     if (rs >= 0) {
       const int l = lo[rs], hh = hi[rs], rc = rch[rs], cu = cum[rs];
-      ccnt = rc + min((hh - l + 32) >> 5, ((X - l) >> 5) + 1);
+      const int w = hh - l + 1;
+      const bool tails = P.slash_tile != 1 && P.n <= MINF_PACK_MAX_N;
+      ccnt = rc + min(tails ? (w >> 5) : ((w + 31) >> 5), ((X - l) >> 5) + 1);
       const int e = min(hh, X), s = max(l, 0);
       cov_pos = cu + (e >= s ? e - s + 1 : 0);
     }
     ccnt = min<long long>(ccnt, P.max_chunks);
+    // packed tail chunks whose first entry is <= 64u
+    const int32_t* tx = P.t.tail_x + (size_t)bh * P.max_tail;
+    const int npk = ok ? (int)min<long long>((P.t.tail_cnt[bh] + 31) >> 5, P.max_tail >> 5) : 0;
+    const int pk = wave_last_le(tx, npk, X, 32) + 1;
     // span edges: Lu per covered x >= 0 with x <= 64u, and max(0, Lu + x)
     // for x in [-63, -1] (lane l takes x = l - 63)
     if (lane == 0) {
       edges += (long long)Lu * cov_pos;
       P.t.chunk_cnt[bu] = ccnt;
+      P.t.pk_cnt[bu] = pk;
     }
     if (nr > 0 && lane < 63) {
       const int x = lane - 63;

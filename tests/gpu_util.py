@@ -186,18 +186,46 @@ def check_tiles(p, res, buf):
             got[a + 63:e + 64] = True
         assert np.array_equal(got, cover), f"span set of head ({b},{h})"
         assert np.all(lo[1:] > hi[:-1] + 1), "spans not disjoint / merged"
+        # the whole 32-offset chunks (ascending) and the packed tail offsets
+        # hold each span offset once; block u uses the chunks and packed
+        # chunks that start at or below 64u, which hold every span offset
+        # x <= 64u
         clo, chi = t["chunk_lo"][b, h], t["chunk_hi"][b, h]
         used = int(t["chunk_cnt"][b, h, nq - 1])      # chunks of the last block
-        got2 = np.zeros_like(cover)
-        for a, e in zip(clo[:used], chi[:used]):
-            assert 0 <= e - a <= 31
-            got2[a + 63:e + 64] = True
         assert np.all(np.diff(clo[:used]) > 0), "chunks not ascending"
+        # tails are packed unless under exact slash pairs (slash_tile == 1)
+        # or beyond MINF_PACK_MAX_N tokens
+        packed = int(sz.bits_words) == 0 and n <= M.MINF_PACK_MAX_N
+        for a, e in zip(clo[:used], chi[:used]):
+            assert (e - a == 31) if packed else (0 <= e - a <= 31), "chunk width"
+        tcnt = int(t["tail_cnt"][b, h])
+        tx = t["tail_x"][b, h]
+        if not packed:
+            assert tcnt == 0, "unpacked tails stay chunks of their own"
+        assert np.all(np.diff(tx[:tcnt]) > 0), "tail offsets not ascending"
+        npk = (tcnt + 31) // 32
+        assert np.all(tx[tcnt:32 * npk] == M.MINF_TAIL_PAD), "tail padding"
+        chunk_x = np.concatenate([np.arange(a, e + 1) for a, e in zip(clo[:used], chi[:used])] +
+                                 [np.zeros(0, np.int64)])
+        both = np.concatenate([chunk_x, tx[:tcnt]])
+        assert len(np.unique(both)) == len(both), "an offset in two chunks"
+        got2 = np.zeros_like(cover)
+        got2[both + 63] = True
         X = 64 * (nq - 1)
         assert not np.any(got2 & ~cover), "a chunk leaves the spans"
         assert np.array_equal(got2[:X + 64], cover[:X + 64]), "chunks miss part of the spans"
         nch = np.array([int(np.sum(clo[:used] <= 64 * u)) for u in range(nq)])
         assert np.array_equal(t["chunk_cnt"][b, h].astype(np.int64), nch), "chunk counts"
+        firsts = tx[0:32 * npk:32]
+        npk_u = np.array([int(np.sum(firsts <= 64 * u)) for u in range(nq)])
+        assert np.array_equal(t["pk_cnt"][b, h].astype(np.int64), npk_u), "packed chunk counts"
+        # every covered offset x <= 64u lies in a chunk or packed chunk that
+        # block u uses
+        cl = np.concatenate([[0], np.cumsum(chi[:used] - clo[:used] + 1)])
+        for u in range(nq):
+            act = np.concatenate([chunk_x[:cl[nch[u]]], tx[:min(tcnt, 32 * npk_u[u])]])
+            want = np.nonzero(cover[:64 * u + 64])[0] - 63
+            assert np.all(np.isin(want, act)), f"block {u} misses a span offset"
         cols = np.asarray(r.cols, dtype=np.int64)
         for u in range(nq):
             end = min(64 * u + 63, n - 1)

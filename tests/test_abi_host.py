@@ -38,8 +38,8 @@ def test_exports_every_declared_symbol(lib):
 def test_struct_layouts_match_header():
     assert ctypes.sizeof(M.MinfProblem) == 40
     assert ctypes.sizeof(M.MinfHeadCfg) == 32
-    assert ctypes.sizeof(M.MinfSizes) == 56
-    assert ctypes.sizeof(M.MinfTiles) == 96
+    assert ctypes.sizeof(M.MinfSizes) == 64
+    assert ctypes.sizeof(M.MinfTiles) == 120
 
 
 def _prob(**kw):
@@ -60,6 +60,9 @@ def test_query_sizes(lib):
     assert s.max_chunks == (1000 + 63 + 31) // 32 + 1000 + 1
     assert s.ws_bytes > 0
     assert s.bits_words == 0        # only for exact slash pairs
+    # span tails: at most 31 offsets per range and at most n + 63 offsets in
+    # all, in whole packed chunks of 32
+    assert s.max_tail == 1088       # min(31 * 1000, 1000 + 63) rounded up to 32
 
 
 def test_query_sizes_exact_slash_pairs(lib):
@@ -125,12 +128,19 @@ def test_calls_reject_before_launch(lib):
     assert "tile" in lib.minf_last_error().decode()
     # exact slash pairs need the two bitmaps
     p1 = _prob(slash_tile=1)
-    ts = M.MinfTiles(*([fake] * 10 + [None, None]))
+    ts = M.MinfTiles(*([fake] * 10 + [None, None] + [fake] * 3))
     st = lib.minf_build_tiles(ctypes.byref(p1), h, fake, fake, fake, fake, ctypes.byref(ts), fake, 1 << 40, None)
     assert st == M.MINF_EINVAL and "slash_bits" in lib.minf_last_error().decode()
     st = lib.minf_sparse_attn(ctypes.byref(p1), h, fake, fake, fake, fake, fake, ctypes.byref(ts), fake, None,
                               fake, 1 << 40, None)
     assert st == M.MINF_EINVAL and "slash_bits" in lib.minf_last_error().decode()
+    # a Vertical-Slash head needs the tail list and the packed-chunk counts
+    ts = M.MinfTiles(*([fake] * 12 + [None, fake, fake]))
+    st = lib.minf_build_tiles(ctypes.byref(p), h, fake, fake, fake, fake, ctypes.byref(ts), fake, 1 << 40, None)
+    assert st == M.MINF_EINVAL and "tail" in lib.minf_last_error().decode()
+    st = lib.minf_sparse_attn(ctypes.byref(p), h, fake, fake, fake, fake, fake, ctypes.byref(ts), fake, None,
+                              fake, 1 << 40, None)
+    assert st == M.MINF_EINVAL
 
 
 def test_static_attention_refuses_oversized_problems(lib):
