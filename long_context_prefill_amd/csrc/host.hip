@@ -119,13 +119,14 @@ struct Carve {
   size_t take(size_t bytes) { size_t o = off; off += (bytes + 255) & ~size_t(255); return o; }
 };
 
-struct TilesWs { size_t span_cum, range_chunks, bitmap, head_ok, total; };
+struct TilesWs { size_t span_cum, range_chunks, range_tails, bitmap, head_ok, total; };
 TilesWs tiles_ws(const minf_problem* p, const Derived& d) {
   Carve c;
   TilesWs w;
   const size_t BH = (size_t)p->B * p->Hq;
   w.span_cum = c.take(BH * (d.max_s + 1) * 4);
   w.range_chunks = c.take(BH * (d.max_s + 1) * 4);
+  w.range_tails = c.take(BH * (d.max_s + 1) * 4);
   w.bitmap = c.take(BH * d.bm_words * 4);
   w.head_ok = c.take(BH * 4);
   w.total = c.off;
@@ -364,6 +365,7 @@ minf_status minf_build_tiles(const minf_problem* prob, const minf_head_cfg* head
   t.t = *tiles;
   t.span_cum = reinterpret_cast<int32_t*>(base + w.span_cum);
   t.range_chunks = reinterpret_cast<int32_t*>(base + w.range_chunks);
+  t.range_tails = reinterpret_cast<int32_t*>(base + w.range_tails);
   t.bitmap = reinterpret_cast<uint32_t*>(base + w.bitmap);
   t.head_ok = reinterpret_cast<int32_t*>(base + w.head_ok);
   t.max_v = d.max_v; t.max_s = d.max_s; t.max_kb = d.max_kb; t.max_chunks = d.max_chunks; t.bm_words = d.bm_words;

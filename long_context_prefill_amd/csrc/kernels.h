@@ -175,6 +175,7 @@ struct TileParams {
   minf_tiles t;
   int32_t* span_cum;         // ws [B,Hq,max_s+1]: covered offsets >= 0 before range r
   int32_t* range_chunks;     // ws [B,Hq,max_s+1]: chunks before range r
+  int32_t* range_tails;      // ws [B,Hq,max_s+1]: tail-list entries before range r
   uint32_t* bitmap;          // ws [B,Hq,bm_words]: bit x+63 set iff x in S
   int32_t* head_ok;          // ws [B,Hq]
   int64_t max_v, max_s, max_kb, max_chunks, bm_words, max_tail;

@@ -167,20 +167,33 @@ __global__ __launch_bounds__(256) void vs_ranges_kernel(TileParams P) {
   if (threadIdx.x == 0) P.t.span_cnt[bh] = ok ? carry : 0;
 }
 
+// Last index r in [0, cnt) with a[r] <= x (a ascending), -1 if none: one
+// thread's binary search.
+__device__ __forceinline__ int last_le(const int32_t* a, int cnt, int x) {
+  int l = 0, r = cnt;
+  while (l < r) { const int m = (l + r) >> 1; if (a[m] <= x) l = m + 1; else r = m; }
+  return l - 1;
+}
+
+constexpr int kSlabWords = 8192;   // bitmap words built in LDS at a time (32 per thread)
+
+// Bits [s, e] (0 <= s <= e <= 31) of a 32-bit word.
+__device__ __forceinline__ uint32_t bit_span(int s, int e) {
+  return (e - s + 1 == 32) ? 0xffffffffu : (((1u << (e - s + 1)) - 1u) << s);
+}
+
 // 2) cut ranges into chunks, prefix counts, coverage bitmap.  Each range is
 //    cut into whole 32-offset chunks from its low end; the shorter last
 //    piece (its tail) goes to the per-head tail list, whose entries the
 //    attention packs 32 to a chunk (under exact slash pairs the tail stays a
 //    chunk of its own: the per-pair test needs contiguous keys; so it does
 //    beyond MINF_PACK_MAX_N tokens, where the walk's locality matters more
-//    than the partial chunks).  The bitmap
-//    is assembled in LDS, kSlabWords words at a time: a range is at least 64
-//    bits wide, so a word meets at most two ranges and every word is written
-//    once, whole.
-constexpr int kSlabWords = 8192;
+//    than the partial chunks).  The chunks, the tail entries and the bitmap
+//    words are written by all threads evenly: each takes a contiguous share
+//    of them, finds its first range once and walks on, so a long range does
+//    not fall to one thread.
 __global__ __launch_bounds__(256) void vs_chunks_kernel(TileParams P) {
   __shared__ int sh[256];
-  __shared__ uint32_t slab[kSlabWords];
   const int bh = blockIdx.x;
   const int h = bh % P.Hq;
   if (P.ht.kind[h] != MINF_VSLASH) return;
@@ -190,9 +203,14 @@ __global__ __launch_bounds__(256) void vs_chunks_kernel(TileParams P) {
   const int32_t* hi = P.t.span_hi + (size_t)bh * P.max_s;
   int32_t* cum = P.span_cum + (size_t)bh * (P.max_s + 1);
   int32_t* rch = P.range_chunks + (size_t)bh * (P.max_s + 1);
+  int32_t* rtl = P.range_tails + (size_t)bh * (P.max_s + 1);
   int32_t* clo = P.t.chunk_lo + (size_t)bh * P.max_chunks;
   int32_t* chi = P.t.chunk_hi + (size_t)bh * P.max_chunks;
   int32_t* tx = P.t.tail_x + (size_t)bh * P.max_tail;
+  auto nchunks = [&](int a, int b) { const int w = b - a + 1; return tails ? (w >> 5) : ((w + 31) >> 5); };
+  auto ntail = [&](int a, int b) { return tails ? ((b - a + 1) & 31) : 0; };
+  auto ncov = [&](int a, int b) { return b >= 0 ? b - max(a, 0) + 1 : 0; };
+  // prefix counts of chunks, covered offsets >= 0 and tail entries per range
   int carry_c = 0, carry_x = 0, carry_t = 0;
   for (int base = 0; base < nr; base += kRound) {
     const int r0 = base + (int)threadIdx.x * kIPT;
@@ -203,14 +221,10 @@ __global__ __launch_bounds__(256) void vs_chunks_kernel(TileParams P) {
       a[e] = r < nr ? lo[r] : 0;
       b[e] = r < nr ? hi[r] : -1;
     }
-    // chunks, covered offsets >= 0 and tail entries of each range
-    auto nchunks = [&](int e) { const int w = b[e] - a[e] + 1; return tails ? (w >> 5) : ((w + 31) >> 5); };
-    auto ntail = [&](int e) { return tails ? ((b[e] - a[e] + 1) & 31) : 0; };
-    auto ncov = [&](int e) { return b[e] >= 0 ? b[e] - max(a[e], 0) + 1 : 0; };
     int sc = 0, sx = 0, st = 0;
     #pragma unroll
     for (int e = 0; e < kIPT; ++e) {
-      if (r0 + e < nr) { sc += nchunks(e); sx += ncov(e); st += ntail(e); }
+      if (r0 + e < nr) { sc += nchunks(a[e], b[e]); sx += ncov(a[e], b[e]); st += ntail(a[e], b[e]); }
     }
     int tc, tx_, tt;
     int pc = carry_c + block_exscan(sc, sh, &tc);
@@ -222,53 +236,98 @@ __global__ __launch_bounds__(256) void vs_chunks_kernel(TileParams P) {
       if (r < nr) {
         rch[r] = pc;
         cum[r] = px;
-        const int nch = nchunks(e), nt = ntail(e);
-        for (int m = 0; m < nch; ++m) {
-          const int c = pc + m;
-          if (c < P.max_chunks) {
-            clo[c] = a[e] + 32 * m;
-            chi[c] = min(a[e] + 32 * m + 31, b[e]);
-          }
-        }
-        for (int i = 0; i < nt; ++i)
-          if (pt + i < P.max_tail) tx[pt + i] = a[e] + 32 * nch + i;
-        pc += nch;
-        px += ncov(e);
-        pt += nt;
+        rtl[r] = pt;
+        pc += nchunks(a[e], b[e]);
+        px += ncov(a[e], b[e]);
+        pt += ntail(a[e], b[e]);
       }
     }
     carry_c += tc;
     carry_x += tx_;
     carry_t += tt;
   }
-  // pad the tail list to whole packed chunks
+  if (threadIdx.x == 0) {
+    rch[nr] = carry_c; cum[nr] = carry_x; rtl[nr] = carry_t;
+    if (carry_c > P.max_chunks) atomicOr(P.t.status, MINF_DEV_CAPACITY);
+  }
+  __syncthreads();   // the prefix arrays are read by every thread below
+  const int nthr = (int)blockDim.x, tid = (int)threadIdx.x;
+  // chunks: chunk c of range r (rch[r] <= c < rch[r+1]) holds offsets
+  // lo[r] + 32 (c - rch[r]) .. +31, clipped to the range
+  {
+    const int tot = (int)min<long long>(carry_c, P.max_chunks);
+    const int per = (tot + nthr - 1) / nthr, c0 = tid * per, c1 = min(tot, c0 + per);
+    if (c0 < c1) {
+      int r = last_le(rch, nr, c0);
+      int next = rch[r + 1], a = lo[r], b = hi[r], first = rch[r];
+      for (int c = c0; c < c1; ++c) {
+        while (c >= next) { ++r; first = next; next = rch[r + 1]; a = lo[r]; b = hi[r]; }
+        const int m = c - first;
+        clo[c] = a + 32 * m;
+        chi[c] = min(a + 32 * m + 31, b);
+      }
+    }
+  }
+  // tail entries: entry i of range r (rtl[r] <= i < rtl[r+1]) is the offset
+  // after the range's whole chunks; then the padding to whole packed chunks
   const int tpad = (carry_t + 31) & ~31;
-  for (int i = carry_t + (int)threadIdx.x; i < tpad; i += 256)
-    if (i < P.max_tail) tx[i] = MINF_TAIL_PAD;
+  {
+    const int per = (tpad + nthr - 1) / nthr, i0 = tid * per, i1 = min(tpad, i0 + per);
+    if (i0 < i1) {
+      int r = carry_t > 0 ? last_le(rtl, nr, min(i0, carry_t - 1)) : 0;
+      int next = nr > 0 ? rtl[r + 1] : 0, first = nr > 0 ? rtl[r] : 0;
+      int xs = nr > 0 ? lo[r] + 32 * nchunks(lo[r], hi[r]) : 0;
+      for (int i = i0; i < i1; ++i) {
+        int v = MINF_TAIL_PAD;
+        if (i < carry_t) {
+          while (i >= next) { ++r; first = next; next = rtl[r + 1]; xs = lo[r] + 32 * nchunks(lo[r], hi[r]); }
+          v = xs + (i - first);
+        }
+        if (i < P.max_tail) tx[i] = v;
+      }
+    }
+  }
   if (threadIdx.x == 0) {
     P.t.tail_cnt[bh] = (int)min<long long>(carry_t, P.max_tail);
     if (tpad > P.max_tail) atomicOr(P.t.status, MINF_DEV_CAPACITY);
   }
-  if (threadIdx.x == 0) { rch[nr] = carry_c; cum[nr] = carry_x; }
-  if (threadIdx.x == 0 && carry_c > P.max_chunks) atomicOr(P.t.status, MINF_DEV_CAPACITY);
-  // coverage bitmap over x in [-63, n): bit (x + 63)
+  // coverage bitmap over x in [-63, n): bit x + 63.  Word w holds bits
+  // 32w .. 32w + 31; the ranges meeting it are the first range ending at or
+  // after its first bit and, ranges being at least 64 bits wide, at most the
+  // one after it.  Slabs of kSlabWords words: each thread builds 32
+  // consecutive words in LDS, walking the ranges with the current and the
+  // next one in registers, and the slab is written out whole.
   uint32_t* bm = P.bitmap + (size_t)bh * P.bm_words;
-  for (int64_t w0 = 0; w0 < P.bm_words; w0 += kSlabWords) {
-    const int nw = (int)min<int64_t>(kSlabWords, P.bm_words - w0);
-    for (int w = threadIdx.x; w < nw; w += 256) slab[w] = 0u;
-    __syncthreads();
-    const int64_t b0 = 32 * w0, b1 = b0 + 32 * (int64_t)nw - 1;   // bits of this slab
-    for (int r = threadIdx.x; r < nr; r += 256) {
-      const int64_t s = max<int64_t>((int64_t)lo[r] + 63, b0), e = min<int64_t>((int64_t)hi[r] + 63, b1);
-      for (int64_t w = s >> 5; w <= (e >> 5) && s <= e; ++w) {
-        const int64_t ws = max(s, 32 * w) - 32 * w, we = min(e, 32 * w + 31) - 32 * w;
-        const uint32_t span = (we - ws + 1 == 32) ? 0xffffffffu : (((1u << (we - ws + 1)) - 1u) << ws);
-        atomicOr(&slab[w - w0], span);
+  __shared__ uint32_t slab[kSlabWords];
+  constexpr int kBig = 1 << 29;      // beyond every range
+  for (int64_t s0 = 0; s0 < P.bm_words; s0 += kSlabWords) {
+    const int nw = (int)min<int64_t>(kSlabWords, P.bm_words - s0);
+    const int w0 = 32 * tid;
+    if (w0 < nw) {
+      const int b00 = 32 * (int)(s0 + w0);
+      // first range r with hi[r] + 63 >= b00
+      int l = 0, rr = nr;
+      while (l < rr) { const int m = (l + rr) >> 1; if (hi[m] + 63 < b00) l = m + 1; else rr = m; }
+      int r = l;
+      int la = r < nr ? lo[r] + 63 : kBig, ha = r < nr ? hi[r] + 63 : kBig;
+      int lb = r + 1 < nr ? lo[r + 1] + 63 : kBig, hb = r + 1 < nr ? hi[r + 1] + 63 : kBig;
+      for (int w = w0; w < min(nw, w0 + 32); ++w) {
+        const int b0 = 32 * (int)(s0 + w), b1 = b0 + 31;
+        while (ha < b0) {
+          ++r;
+          la = lb; ha = hb;
+          lb = r + 1 < nr ? lo[r + 1] + 63 : kBig;
+          hb = r + 1 < nr ? hi[r + 1] + 63 : kBig;
+        }
+        uint32_t bits = 0;
+        if (la <= b1) bits |= bit_span(max(la, b0) - b0, min(ha, b1) - b0);
+        if (lb <= b1) bits |= bit_span(max(lb, b0) - b0, min(hb, b1) - b0);
+        slab[w] = bits;
       }
     }
     __syncthreads();
-    for (int w = threadIdx.x; w < nw; w += 256) bm[w0 + w] = slab[w];
-    __syncthreads();   // the slab is cleared again for the next words
+    for (int w = tid; w < nw; w += nthr) bm[s0 + w] = slab[w];
+    __syncthreads();   // the slab is rebuilt for the next words
   }
 }
 
@@ -444,14 +503,12 @@ __global__ __launch_bounds__(256) void vs_exact_edges_kernel(TileParams P) {
   }
 }
 
-// 4) Block-Sparse: validate J_u and count the kept block areas.  One wave
-//    per query block, 64 entries of J_u per round.
+// 4) Block-Sparse: validate J_u and count the kept block areas.
 __global__ __launch_bounds__(256) void bs_edges_kernel(TileParams P) {
   const int bh = blockIdx.y;
   const int h = bh % P.Hq;
   if (P.ht.kind[h] != MINF_BSPARSE) return;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int u = blockIdx.x * 4 + wave;
+  const int u = blockIdx.x * 256 + threadIdx.x;
   __shared__ unsigned long long part[4];
   unsigned long long edges = 0;
   if (u < P.nq) {
@@ -460,20 +517,17 @@ __global__ __launch_bounds__(256) void bs_edges_kernel(TileParams P) {
     const int Lu = min(64, P.n - 64 * u);
     bool bad = cnt < 0 || cnt > P.max_kb || cnt > u + 1;
     const int32_t* J = P.blk_idx + bu * P.max_kb;
-    for (int base = 0; !bad && base < cnt; base += 64) {
-      const int i = base + lane;
-      const int v = i < cnt ? J[i] : 0;
-      const int prev = (i < cnt && i > 0) ? J[i - 1] : -1;
-      if (__any(i < cnt && (v <= prev || v > u))) bad = true;
-      if (i < cnt) edges += (v < u) ? (unsigned long long)Lu * 64ull : (unsigned long long)(Lu * (Lu + 1) / 2);
+    int prev = -1;
+    for (int i = 0; !bad && i < cnt; ++i) {
+      const int v = J[i];
+      if (v <= prev || v > u) { bad = true; break; }
+      edges += (v < u) ? (unsigned long long)Lu * 64ull : (unsigned long long)(Lu * (Lu + 1) / 2);
+      prev = v;
     }
-    if (bad) {
-      if (lane == 0) atomicOr(P.t.status, MINF_DEV_BAD_BLOCK);
-      edges = 0;
-    }
+    if (bad) { atomicOr(P.t.status, MINF_DEV_BAD_BLOCK); edges = 0; }
   }
   for (int off = 32; off > 0; off >>= 1) edges += __shfl_xor(edges, off);
-  if (lane == 0) part[wave] = edges;
+  if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = edges;
   __syncthreads();
   if (threadIdx.x == 0) {
     const unsigned long long tot = part[0] + part[1] + part[2] + part[3];
@@ -492,7 +546,7 @@ hipError_t launch_tiles(const TileParams& p, bool has_vs, bool has_bs, hipStream
       hipLaunchKernelGGL(vs_exact_edges_kernel, dim3(BH), dim3(256), 0, st, p);
     }
   }
-  if (has_bs) hipLaunchKernelGGL(bs_edges_kernel, dim3((p.nq + 3) / 4, BH), dim3(256), 0, st, p);
+  if (has_bs) hipLaunchKernelGGL(bs_edges_kernel, dim3((p.nq + 255) / 256, BH), dim3(256), 0, st, p);
   return hipGetLastError();
 }
 
