@@ -35,13 +35,20 @@ def hipcc():
     raise RuntimeError("hipcc not found")
 
 
+# Per-file flags.  attn_bf16.hip takes the next work item's queue ticket
+# with one lane's atomic during the current item and uses the value only at
+# the item's end; the compiler's atomic optimizer would turn that atomic into
+# a wave-wide reduction whose result is waited for at once.
+FILE_FLAGS = {"attn_bf16.hip": ["-mllvm", "-amdgpu-atomic-optimizer-strategy=None"]}
+
+
 def sources():
     return sorted(os.path.join(CSRC, f) for f in os.listdir(CSRC) if f.endswith(".hip"))
 
 
 def _compile(cc, src, extra):
     obj = os.path.join(OBJDIR, os.path.basename(src)[:-4] + ".o")
-    cmd = [cc] + FLAGS + extra + ["-c", src, "-o", obj]
+    cmd = [cc] + FLAGS + FILE_FLAGS.get(os.path.basename(src), []) + extra + ["-c", src, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"compile failed: {' '.join(cmd)}\n{r.stdout}\n{r.stderr}")

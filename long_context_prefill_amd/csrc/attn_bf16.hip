@@ -61,7 +61,8 @@ constexpr int kTileB = 32 * kRowB;      // 8 KiB: one chunk of K (or V)
 constexpr int kSlotB = 2 * kTileB;      // K then V
 constexpr int kRing = 2 * kSlotB;       // two K/V slots
 constexpr int kListB = 32 * 4;          // one gathered chunk's 32 list entries
-constexpr int kSmem = kRing + 3 * kListB;   // plus a ring of three entry lists
+constexpr int kTicket = kRing + 3 * kListB;  // the next item's queue ticket
+constexpr int kSmem = kTicket + 16;          // K/V ring, entry-list ring, ticket
 constexpr float kTau = 8.0f;
 constexpr float kMInit = -1.0e30f;      // running maximum before any key (finite)
 
@@ -397,9 +398,11 @@ __device__ __forceinline__ void wait_copies_and_barrier() {
 }
 
 // One work item: query block u of head (b, h), both waves of the work-group.
+// The next item's queue ticket is taken from *tkp by thread 0 at the start
+// of this item's last chunk and left in *s_tk after its output stores.
 template <int KIND>
 __device__ __forceinline__ void attn_item(const AttnParams& P, const SampleView& S, const int h, const int u,
-                                          lds_char* smem) {
+                                          lds_char* smem, int* tkp, int* s_tk) {
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int l32 = lane & 31;
@@ -449,6 +452,7 @@ __device__ __forceinline__ void attn_item(const AttnParams& P, const SampleView&
       }
       if (hh == 0 && P.lse) P.lse[hrow + myrow] = kNegInf;
     }
+    if (threadIdx.x == 0) *s_tk = atomicAdd(tkp, 1);
     return;
   }
   const int sink_len = __builtin_amdgcn_readfirstlane(L.sink_len);
@@ -814,6 +818,7 @@ __device__ __forceinline__ void attn_item(const AttnParams& P, const SampleView&
   // iteration 0 rewrites the K half of slot 0, which both waves just read
   wait_copies_and_barrier();
 
+  int tk = 0;   // thread 0: the next item's ticket
   // STEADY: chunks j+1 .. j+3 exist (j+1 .. j+2 for A-shape; no bound tests)
   auto iteration = [&](const int j, const int sl, auto steady, floatx16& s_cur, floatx16& s_nxt) {
     constexpr bool STEADY = decltype(steady)::value;
@@ -824,6 +829,11 @@ __device__ __forceinline__ void attn_item(const AttnParams& P, const SampleView&
     u32x4 kop[8], vop[2][4];
     const bool more = STEADY || j + 1 < C;
     const bool more2 = STEADY || j + 2 < C;
+    // the last chunk: take the next item's ticket now, so that its round trip
+    // (and the item boundary) does not wait for this item's output stores
+    if constexpr (!STEADY) {
+      if (j == C - 1 && threadIdx.x == 0) tk = atomicAdd(tkp, 1);
+    }
     read_k(sl ^ 1, kop);
     if constexpr (kPrefetch) {
       if (more2) {
@@ -922,6 +932,12 @@ __device__ __forceinline__ void attn_item(const AttnParams& P, const SampleView&
     wait_copies_and_barrier();
   }
 
+  // the next ticket, taken at the start of the last chunk, goes to LDS before
+  // the output stores: waiting for it here waits for nothing else (the last
+  // chunk issues no copies), whereas after the stores the wait would include
+  // them (one counter covers loads and stores)
+  if (threadIdx.x == 0) *s_tk = tk;
+
   // ---- finish: the row's sum over both lane halves, O = acc / l, LSE
   const float l_tot = l_run + __shfl_xor(l_run, 32);
   const float f = l_tot > 0.f ? 1.0f / l_tot : 0.f;
@@ -955,15 +971,19 @@ void attn_bf16_d128_kernel(AttnParams P) {
   const int qoff = P.queue_meta[xcd];
   const int qcnt = P.queue_meta[8 + xcd];
   __shared__ __attribute__((aligned(16))) char smem_g[kSmem];
-  // the queue ticket shares the first word of the K ring: it is written and
-  // read between items, when no copy is in flight
-  int& s_next = *reinterpret_cast<int*>(smem_g);
   lds_char* smem = (lds_char*)smem_g;
+  // tickets: the first here, each next one by the item before it (during its
+  // last chunk), published in LDS after that item's output stores.  The
+  // barriers between items wait for LDS only: the output stores complete
+  // while the next item loads its lists.
+  int* s_tk = reinterpret_cast<int*>(smem_g + kTicket);
+  int* tkp = &P.queue_meta[16 + xcd];
+  if (threadIdx.x == 0) *s_tk = atomicAdd(tkp, 1);
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
   while (true) {
-    if (threadIdx.x == 0) s_next = atomicAdd(&P.queue_meta[16 + xcd], 1);
-    __syncthreads();
-    const int qi = __builtin_amdgcn_readfirstlane(s_next);
-    __syncthreads();   // both waves hold qi before the next write of s_next
+    const int qi = __builtin_amdgcn_readfirstlane(*s_tk);
+    // both waves hold qi before the ticket word is written again
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
     if (qi >= qcnt) break;
     const int item = ld_uniform(P.queue, (int64_t)qoff + qi);
     const int bhi = item / P.nq;
@@ -972,10 +992,11 @@ void attn_bf16_d128_kernel(AttnParams P) {
     const int h = bhi % P.Hq;
     const int kind = __builtin_amdgcn_readfirstlane(P.ht.kind[h]);
     const SampleView S = sample_view(P, b);
-    if (kind == MINF_VSLASH) attn_item<MINF_VSLASH>(P, S, h, u, smem);
-    else if (kind == MINF_BSPARSE) attn_item<MINF_BSPARSE>(P, S, h, u, smem);
-    else attn_item<MINF_ASHAPE>(P, S, h, u, smem);
-    __syncthreads();   // the next item reuses the LDS rings
+    if (kind == MINF_VSLASH) attn_item<MINF_VSLASH>(P, S, h, u, smem, tkp, s_tk);
+    else if (kind == MINF_BSPARSE) attn_item<MINF_BSPARSE>(P, S, h, u, smem, tkp, s_tk);
+    else attn_item<MINF_ASHAPE>(P, S, h, u, smem, tkp, s_tk);
+    // the next item reuses the LDS rings and reads the ticket
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
   }
 }
 
