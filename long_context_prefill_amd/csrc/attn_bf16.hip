@@ -158,7 +158,9 @@ __device__ __forceinline__ ItemLists item_lists(const AttnParams& P, const Sampl
 //   blocks are queued from the last to the first;
 // * a Block-Sparse unit holds every Block-Sparse head of one (batch, KV
 //   group) over such a run, interleaved per query block: heads that share K
-//   and V and select nearly the same key blocks run side by side.
+//   and V and select nearly the same key blocks run side by side.  Beyond
+//   kGroupAllMinN tokens the Vertical-Slash and A-shape heads of a group
+//   are grouped the same way (group_kinds).
 // Units are costed by their exact chunk counts.  KV groups are taken in
 // order, and within a group the units are handed out largest first, eight
 // at a time, to the eight XCD queues in ascending order of load, so the
@@ -168,26 +170,28 @@ __device__ __forceinline__ ItemLists item_lists(const AttnParams& P, const Sampl
 // one head (or one KV group), whose key sets largely coincide, so their K/V
 // rows are also shared in that XCD's L2.
 
-// Block-Sparse heads of h's KV group: their number, and h's rank among them.
-__device__ __forceinline__ int bs_group(const AttnParams& P, int h, int* rank) {
-  const int g0 = (h / P.gsz) * P.gsz;
+// Heads of h's KV group with h's pattern kind: their number, and h's rank
+// among them.
+__device__ __forceinline__ int kind_group(const AttnParams& P, int h, int* rank) {
+  const int g0 = (h / P.gsz) * P.gsz, kind = P.ht.kind[h];
   int cnt = 0, r = -1;
   for (int k = g0; k < g0 + P.gsz; ++k) {
-    if (P.ht.kind[k] != MINF_BSPARSE) continue;
+    if (P.ht.kind[k] != kind) continue;
     if (k == h) r = cnt;
     ++cnt;
   }
   *rank = r;
   return cnt;
 }
-// k-th Block-Sparse head of the KV group that starts at head g0
-__device__ __forceinline__ int bs_head(const AttnParams& P, int g0, int k) {
+// k-th head of the given kind in the KV group that starts at head g0
+__device__ __forceinline__ int kind_head(const AttnParams& P, int g0, int k, int kind) {
   for (int j = g0; j < g0 + P.gsz; ++j)
-    if (P.ht.kind[j] == MINF_BSPARSE && k-- == 0) return j;
+    if (P.ht.kind[j] == kind && k-- == 0) return j;
   return g0;
 }
-// Items of a unit (0 for the units of Block-Sparse heads other than the
-// first of their group, whose items the first head's unit carries).
+__device__ __forceinline__ bool grouped(const AttnParams& P, int kind) { return (P.group_kinds >> kind) & 1; }
+// Items of a unit (0 for the units of grouped heads other than the first of
+// their kind in their group, whose items the first head's unit carries).
 __device__ __forceinline__ int unit_items(const AttnParams& P, int unit, int* u0, int* u1, int* nbs) {
   const int bhi = unit / P.sched_P, part = unit % P.sched_P;
   const int h = bhi % P.Hq;
@@ -196,9 +200,9 @@ __device__ __forceinline__ int unit_items(const AttnParams& P, int unit, int* u0
   *u1 = min(*u0 + P.sched_R, nq);
   *nbs = 1;
   if (*u0 >= *u1) return 0;
-  if (P.ht.kind[h] == MINF_BSPARSE) {
+  if (grouped(P, P.ht.kind[h])) {
     int r;
-    *nbs = bs_group(P, h, &r);
+    *nbs = kind_group(P, h, &r);
     if (r != 0) return 0;
     return (*u1 - *u0) * *nbs;
   }
@@ -216,7 +220,7 @@ __global__ __launch_bounds__(256) void attn_cost_kernel(AttnParams P) {
   long long c = 0;
   for (int i = (int)threadIdx.x; i < items; i += 256) {
     const int u = u1 - 1 - i / nbs;
-    const int hh = kind == MINF_BSPARSE ? bs_head(P, (h / P.gsz) * P.gsz, i % nbs) : h;
+    const int hh = grouped(P, kind) ? kind_head(P, (h / P.gsz) * P.gsz, i % nbs, kind) : h;
     const ItemLists L = item_lists(P, S, hh, kind, u);
     c += L.Ca + L.Cb + 2;   // + fixed cost of an item (Q load, output)
   }
@@ -323,11 +327,12 @@ __global__ __launch_bounds__(256) void attn_fill_kernel(AttnParams P) {
   const int items = unit_items(P, unit, &u0, &u1, &nbs);
   const int bhi = unit / P.sched_P;
   const int b = bhi / P.Hq, h = bhi % P.Hq;
-  const bool bs = P.ht.kind[h] == MINF_BSPARSE;
+  const int kind = P.ht.kind[h];
+  const bool grp = grouped(P, kind);
   int32_t* q = P.queue + P.queue_meta[x] + P.unit_off[unit];
   for (int i = (int)threadIdx.x; i < items; i += 256) {
     const int u = u1 - 1 - i / nbs;
-    const int hh = bs ? bs_head(P, (h / P.gsz) * P.gsz, i % nbs) : h;
+    const int hh = grp ? kind_head(P, (h / P.gsz) * P.gsz, i % nbs, kind) : h;
     q[i] = ((b * P.Hq + hh) * P.nq) + u;
   }
 }

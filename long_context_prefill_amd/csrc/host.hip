@@ -410,6 +410,7 @@ static minf_status attn_launch(const minf_problem* prob, const Derived& d, const
   a.queue = reinterpret_cast<int32_t*>(wb + w.queue);
   a.queue_meta = reinterpret_cast<int32_t*>(wb + w.meta);
   a.sched_P = w.P; a.sched_R = w.R; a.sched_units = w.units;
+  a.group_kinds = minf::group_kinds(prob->n);
   a.Q = Q; a.K = K; a.V = V; a.O = O; a.lse = lse;
   a.blk_idx = blk_idx; a.blk_cnt = blk_cnt;
   if (d.has_vs && !samples) {
