@@ -64,12 +64,8 @@ typedef enum { MINF_ASHAPE = 0, MINF_VSLASH = 1, MINF_BSPARSE = 2 } minf_kind;
 enum { MINF_FORCE_FIRST_BLOCK = 1, MINF_FORCE_DIAG_BLOCK = 2 };
 enum { MINF_MAX_HEADS = 64, MINF_BLOCK = 64, MINF_MAX_LAST_Q = 64, MINF_CHUNK = 32 };
 /* Offset that pads the tail list of minf_tiles: 64u - MINF_TAIL_PAD is
- * negative for every block, so a padding entry covers no key.  Span tails
- * are packed only for sequences of at most MINF_PACK_MAX_N tokens (measured:
- * faster at 32K and 128K; slower at 1M, where the attention is bound by
- * memory traffic and packed chunks gather scattered rows); longer sequences
- * keep every range's tail as a chunk of its own and an empty tail list. */
-enum { MINF_TAIL_PAD = 1 << 30, MINF_PACK_MAX_N = 1 << 18 };
+ * negative for every block, so a padding entry covers no key. */
+enum { MINF_TAIL_PAD = 1 << 30 };
 
 /* One query head's entry in the layer's pattern table (MInference page,
  * section 6.3: pattern kind, vertical count, slash count, block count,
@@ -134,9 +130,8 @@ typedef struct {
  *                     (chunk_hi - chunk_lo = 31), ascending.  For block u a
  *                     chunk covers the 32 contiguous keys
  *                     [64u - chunk_hi, 64u - chunk_lo].  Under slash_tile == 1
- *                     or for n > MINF_PACK_MAX_N a range's last, shorter piece
- *                     is listed here too (chunk_hi - chunk_lo <= 31) and the
- *                     tail list is empty.
+ *                     a range's last, shorter piece is listed here too
+ *                     (chunk_hi - chunk_lo <= 31) and the tail list is empty.
  *   chunk_cnt         [B, Hq, nq]         chunks of block u: those whose
  *                     chunk_lo <= 64u (the others lie before key 0).
  *   tail_x            [B, Hq, max_tail]   the offsets x of every range's last

@@ -36,7 +36,7 @@ MINF_ASHAPE, MINF_VSLASH, MINF_BSPARSE = 0, 1, 2
 MINF_FORCE_FIRST_BLOCK, MINF_FORCE_DIAG_BLOCK = 1, 2
 MINF_DEV_BAD_VERTICAL, MINF_DEV_BAD_SLASH, MINF_DEV_BAD_BLOCK, MINF_DEV_CAPACITY = 1, 2, 4, 8
 MINF_DEV_WAIT_EXHAUSTED = 16
-MINF_TAIL_PAD, MINF_PACK_MAX_N = 1 << 30, 1 << 18
+MINF_TAIL_PAD = 1 << 30
 
 EXPORTED = ["minf_query_sizes", "minf_vs_index", "minf_vs_index_fused", "minf_bs_index", "minf_build_tiles",
             "minf_sparse_attn", "minf_sparse_attn_static", "minf_output_error", "minf_captured_mass", "minf_ragged_ws_bytes",

@@ -186,10 +186,9 @@ __device__ __forceinline__ uint32_t bit_span(int s, int e) {
 //    cut into whole 32-offset chunks from its low end; the shorter last
 //    piece (its tail) goes to the per-head tail list, whose entries the
 //    attention packs 32 to a chunk (under exact slash pairs the tail stays a
-//    chunk of its own: the per-pair test needs contiguous keys; so it does
-//    beyond MINF_PACK_MAX_N tokens, where the walk's locality matters more
-//    than the partial chunks).  The chunks, the tail entries and the bitmap
-//    words are written by all threads evenly: each takes a contiguous share
+//    chunk of its own: the per-pair test needs contiguous keys).  The
+//    chunks, the tail entries and the bitmap words are written by all
+//    threads evenly: each takes a contiguous share
 //    of them, finds its first range once and walks on, so a long range does
 //    not fall to one thread.
 __global__ __launch_bounds__(256) void vs_chunks_kernel(TileParams P) {
@@ -197,7 +196,7 @@ __global__ __launch_bounds__(256) void vs_chunks_kernel(TileParams P) {
   const int bh = blockIdx.x;
   const int h = bh % P.Hq;
   if (P.ht.kind[h] != MINF_VSLASH) return;
-  const bool tails = P.slash_tile != 1 && P.n <= MINF_PACK_MAX_N;
+  const bool tails = P.slash_tile != 1;
   const int nr = P.t.span_cnt[bh];
   const int32_t* lo = P.t.span_lo + (size_t)bh * P.max_s;
   const int32_t* hi = P.t.span_hi + (size_t)bh * P.max_s;
@@ -367,7 +366,7 @@ __global__ __launch_bounds__(256) void vs_cols_kernel(TileParams P) {
     if (rs >= 0) {
       const int l = lo[rs], hh = hi[rs], rc = rch[rs], cu = cum[rs];
       const int w = hh - l + 1;
-      const bool tails = P.slash_tile != 1 && P.n <= MINF_PACK_MAX_N;
+      const bool tails = P.slash_tile != 1;
       ccnt = rc + min(tails ? (w >> 5) : ((w + 31) >> 5), ((X - l) >> 5) + 1);
       const int e = min(hh, X), s = max(l, 0);
       cov_pos = cu + (e >= s ? e - s + 1 : 0);

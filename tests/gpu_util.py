@@ -194,8 +194,7 @@ def check_tiles(p, res, buf):
         used = int(t["chunk_cnt"][b, h, nq - 1])      # chunks of the last block
         assert np.all(np.diff(clo[:used]) > 0), "chunks not ascending"
         # tails are packed unless under exact slash pairs (slash_tile == 1)
-        # or beyond MINF_PACK_MAX_N tokens
-        packed = int(sz.bits_words) == 0 and n <= M.MINF_PACK_MAX_N
+        packed = int(sz.bits_words) == 0
         for a, e in zip(clo[:used], chi[:used]):
             assert (e - a == 31) if packed else (0 <= e - a <= 31), "chunk width"
         tcnt = int(t["tail_cnt"][b, h])
