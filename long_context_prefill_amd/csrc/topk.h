@@ -74,10 +74,38 @@ __device__ __forceinline__ void pick_digit(int tot, int rem, uint32_t prefix, ui
   __syncthreads();
 }
 
+// Adds one to hist[bin] for every lane with act set.  The keys of one row
+// tend to share their top bytes, so most lanes of a wave fall into one or
+// two bins, and plain atomics would queue on those counters: the lanes of
+// the first two distinct bins (in lane order) are counted with one atomic
+// each, the remaining lanes add their own one.
+__device__ __forceinline__ void hist_add(int* hist, bool act, uint32_t bin) {
+  const int lane = threadIdx.x & 63;
+  uint64_t am = __ballot(act);
+  #pragma unroll
+  for (int it = 0; it < 2; ++it) {
+    if (am == 0) return;
+    const int lead = __ffsll((unsigned long long)am) - 1;
+    const uint32_t lb = (uint32_t)__builtin_amdgcn_readlane((int)bin, lead);
+    const uint64_t m = __ballot(act && bin == lb);
+    if (lane == lead) atomicAdd(&hist[lb], __popcll(m));
+    if ((m >> lane) & 1ull) act = false;
+    am &= ~m;
+  }
+  if (act) atomicAdd(&hist[bin], 1);
+}
+
 // Selects the top min(k, n) of get(0..n-1), up to NT * E elements held in
 // registers, and writes their indices, ascending, to out[0..); out[min(k,n)
 // .. cap) is filled with -1.  Thread t reads elements [t*E, t*E + E) once;
-// the four radix passes and the ordered compaction work on those registers.  `get(i)` is called once per element.
+// the four radix passes and the ordered compaction work on those registers.
+// `get(i)` is called once for every i < NT * E (also past n, where its value
+// is discarded), must be safe to call there and must not return NaN.  Slots past
+// n hold key 0, below the key of every other float (-inf has key
+// 0x007fffff): they can only fall into the lowest bin of a pass whose prefix
+// is all zero, below every real key, so the k <= n largest keys, the
+// threshold and the selection do not depend on them and no pass tests for
+// them.
 struct TopkRegShared {
   int hist[4][256];
   int scan[17];
@@ -106,17 +134,29 @@ __device__ void block_topk_reg(Get get, int n, int k, int32_t* __restrict__ out,
   }
   uint32_t key[E];
   #pragma unroll
-  for (int e = 0; e < E; ++e) key[e] = (lo + e < n) ? order_key(get(lo + e)) : 0u;
-  if (tid == 0) { sh.prefix = 0; sh.mask = 0; sh.remaining = k; }
+  for (int e = 0; e < E; ++e) {
+    const uint32_t x = order_key(get(lo + e));
+    key[e] = lo + e < n ? x : 0u;
+  }
+  for (int i = tid; i < 4 * 256; i += NT) sh.hist[i >> 8][i & 255] = 0;
   __syncthreads();
-  for (int shift = 24; shift >= 0; shift -= 8) {
+  // first digit: every key takes part
+  #pragma unroll
+  for (int e = 0; e < E; ++e) atomicAdd(&sh.hist[wave][key[e] >> 24], 1);
+  __syncthreads();
+  pick_digit(sh.hist[0][tid] + sh.hist[1][tid] + sh.hist[2][tid] + sh.hist[3][tid], k, 0u, 0u, 24, sh.scan,
+             &sh.prefix, &sh.mask, &sh.remaining);
+  for (int shift = 16; shift >= 0; shift -= 8) {
     for (int i = tid; i < 4 * 256; i += NT) sh.hist[i >> 8][i & 255] = 0;
     __syncthreads();
     const uint32_t prefix = sh.prefix, mask = sh.mask;
     const int rem = sh.remaining;
+    // later digits: few keys still match, so a wave with none skips
     #pragma unroll
-    for (int e = 0; e < E; ++e)
-      if (lo + e < n && (key[e] & mask) == prefix) atomicAdd(&sh.hist[wave][(key[e] >> shift) & 255u], 1);
+    for (int e = 0; e < E; ++e) {
+      const bool mt = (key[e] & mask) == prefix;
+      if (__ballot(mt) != 0ull && mt) atomicAdd(&sh.hist[wave][(key[e] >> shift) & 255u], 1);
+    }
     __syncthreads();
     const int tot = sh.hist[0][tid] + sh.hist[1][tid] + sh.hist[2][tid] + sh.hist[3][tid];
     pick_digit(tot, rem, prefix, mask, shift, sh.scan, &sh.prefix, &sh.mask, &sh.remaining);
@@ -125,8 +165,7 @@ __device__ void block_topk_reg(Get get, int n, int k, int32_t* __restrict__ out,
   const int need_eq = sh.remaining;     // elements equal to T that are taken
   int n_gt = 0, n_eq = 0;
   #pragma unroll
-  for (int e = 0; e < E; ++e)
-    if (lo + e < n) { n_gt += key[e] > T; n_eq += key[e] == T; }
+  for (int e = 0; e < E; ++e) { n_gt += key[e] > T; n_eq += key[e] == T; }
   int tot_eq;
   const int eq_rank0 = block_scan_excl<NT>(n_eq, sh.scan, &tot_eq);
   const int take_eq = max(0, min(n_eq, need_eq - eq_rank0));
@@ -135,11 +174,9 @@ __device__ void block_topk_reg(Get get, int n, int k, int32_t* __restrict__ out,
   int eq_seen = 0;
   #pragma unroll
   for (int e = 0; e < E; ++e) {
-    if (lo + e < n) {
-      bool sel = key[e] > T;
-      if (!sel && key[e] == T) { sel = eq_seen < take_eq; ++eq_seen; }
-      if (sel) out[pos++] = lo + e;
-    }
+    bool sel = key[e] > T;
+    if (!sel && key[e] == T) { sel = eq_seen < take_eq; ++eq_seen; }
+    if (sel) out[pos++] = lo + e;
   }
   for (int i = k + tid; i < cap; i += NT) out[i] = -1;
   __syncthreads();

@@ -726,7 +726,7 @@ __global__ __launch_bounds__(256) void vs_tk_pass_kernel(VsParams P, int shift) 
   const int32_t* st = reinterpret_cast<const int32_t*>(P.ws_base + P.ws.tk_state) + 4 * a;
   int32_t* ghist = reinterpret_cast<int32_t*>(P.ws_base + P.ws.tk_hist) + ((size_t)a * P.ws.tk_segs + seg) * 256;
   __shared__ int hist[4][256];
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int tid = threadIdx.x, wave = tid >> 6;
   for (int i = tid; i < 4 * 256; i += 256) hist[i >> 8][i & 255] = 0;
   const uint32_t prefix = (uint32_t)st[0], mask = (uint32_t)st[1];
   __syncthreads();
@@ -743,19 +743,7 @@ __global__ __launch_bounds__(256) void vs_tk_pass_kernel(VsParams P, int shift) 
   for (int e = 0; e < E; ++e) {
     const uint32_t key = order_key(x[e]);
     const bool m = lo + tid + 256 * e < hi && (key & mask) == prefix;
-    const uint32_t d = (key >> shift) & 255u;
-    // scores of one array cluster in few bins: when every counted lane of
-    // the wave has the same digit, one lane adds them all
-    const unsigned long long act = __ballot(m);
-    if (act == 0ull) continue;
-    const int first = __builtin_ctzll(act);
-    const uint32_t d0 = (uint32_t)__builtin_amdgcn_readlane((int)d, first);
-    const unsigned long long same = __ballot(m && d == d0);
-    if (same == act) {
-      if (lane == first) atomicAdd(&hist[wave][d0], (int)__popcll(act));
-    } else if (m) {
-      atomicAdd(&hist[wave][d], 1);
-    }
+    hist_add(hist[wave], m, (key >> shift) & 255u);
   }
   __syncthreads();
   ghist[tid] = hist[0][tid] + hist[1][tid] + hist[2][tid] + hist[3][tid];
