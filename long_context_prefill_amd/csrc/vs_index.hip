@@ -92,13 +92,36 @@ struct ProxyOps {
   }
 };
 
+// Adds src of lane (l + N) (DPP row_shl:N) or lane (l - N) (row_shr:N) within
+// each row of 16 lanes; lanes whose source lies outside the row add 0.
+template <int CTRL>
+__device__ __forceinline__ float dpp_in_row(float src) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, src), CTRL, 0xf, 0xf, true));
+}
+constexpr int kRowShl = 0x100, kRowShr = 0x110;
+
 // PASS 1: per-row running (max, sum) partials.  PASS 2: probabilities,
 // column sums and diagonal partials.
 // grid (key ranges, B*Hq): one work-group per 1024 consecutive keys of one
-// query head; the ranges of a head are dispatched in order.
+// query head; the ranges of a head are dispatched in order.  Each wave walks
+// its 256 keys in 8 steps of 32; the keys of the next step are loaded while
+// the current step is computed.
+//
+// Diagonal sums in registers (pass 2): in a 16x16 product tile, lane (c, g)
+// holds p(row c, key 4g + i), i = 0..3, and lanes 16g .. 16g + 15 form one
+// DPP row.  Shifting register i by i lanes (lane c reads lane c + i) puts
+// p(row c + i, key 4g + i) in lane c: all four share the offset c - 4g, so
+// one add chain per tile sums a diagonal piece; the values whose row c + i
+// passes 15 (read with the opposite shift by 16 - i) lie on the offset 16
+// lower.  With the step and the tile's (row, key) block the offset is
+// base + 16 M + c - 4g, and each lane keeps one partial per M (20 of them
+// for the wave's 8 steps); at the end the four lanes (one per g) of every
+// offset are added in a fixed order through LDS.
 template <typename T, int DH, int PASS>
 __global__ __launch_bounds__(256) void vs_proxy_kernel(VsParams P) {
   using Ops = ProxyOps<T, DH>;
+  constexpr int kSteps = kVsWaveKeys / 32;
+  constexpr int kM = 2 * kSteps + 4;        // diagonal partials per lane
   const int gsz = P.Hq / P.Hkv;
   const int bh = blockIdx.y;
   const int range = blockIdx.x;
@@ -130,23 +153,32 @@ __global__ __launch_bounds__(256) void vs_proxy_kernel(VsParams P) {
   for (int nb = 0; nb < 4; ++nb) { m_run[nb] = kNegInf; l_run[nb] = 0.f; lse2[nb] = 0.f; }
   float* cdst = P.vert_score ? P.vert_score : reinterpret_cast<float*>(P.ws_base + P.ws.cbuf);
   cdst += (size_t)bh * n;
-  float dslot[5] = {0.f, 0.f, 0.f, 0.f, 0.f};
-  __shared__ float ptile[4][64][33];
+  float dacc[kM];
+  #pragma unroll
+  for (int i = 0; i < kM; ++i) dacc[i] = 0.f;
   if constexpr (PASS == 2) {
     const float* l2 = reinterpret_cast<const float*>(P.ws_base + P.ws.lse2) + (size_t)bh * 64;
     #pragma unroll
     for (int nb = 0; nb < 4; ++nb) lse2[nb] = l2[16 * nb + r16];
   }
 
-  for (int j = J0, step = 0; j < J1; j += 32, ++step) {
-    typename Ops::QOp kop[2][Ops::KS];
-    #pragma unroll
-    for (int hh = 0; hh < 2; ++hh) Ops::load_k(Kb, min(j + 16 * hh + r16, n - 1), g, kop[hh]);
+  typename Ops::QOp kop[2][2][Ops::KS];
+  #pragma unroll
+  for (int hh = 0; hh < 2; ++hh) Ops::load_k(Kb, min(J0 + 16 * hh + r16, n - 1), g, kop[0][hh]);
+  #pragma unroll
+  for (int step = 0; step < kSteps; ++step) {
+    const int j = J0 + 32 * step;
+    if (j >= J1) break;
+    auto& kc = kop[step & 1];
+    if (step + 1 < kSteps) {
+      #pragma unroll
+      for (int hh = 0; hh < 2; ++hh) Ops::load_k(Kb, min(j + 32 + 16 * hh + r16, n - 1), g, kop[(step + 1) & 1][hh]);
+    }
     floatx4 s[2][4];
     #pragma unroll
     for (int hh = 0; hh < 2; ++hh)
       #pragma unroll
-      for (int nb = 0; nb < 4; ++nb) s[hh][nb] = Ops::dot(kop[hh], q[nb]);
+      for (int nb = 0; nb < 4; ++nb) s[hh][nb] = Ops::dot(kc[hh], q[nb]);
     // valid pairs: sampled row r < L, key < n, key <= query index
     const bool need_mask = (L < 64) || (j + 31 > row_base);
     if (need_mask) {
@@ -215,32 +247,22 @@ __global__ __launch_bounds__(256) void vs_proxy_kernel(VsParams P) {
         const int key = j + 16 * hh + 4 * g + i;
         if (key < n) cdst[key] = val;
       }
-      // diagonal partials: tile[r][jl] = p(row r, key j + jl)
+      // diagonal pieces of the 8 tiles: tile (nb, hh) has offsets
+      // base + 16 (nb - hh - 2 step) + r16 - 4g (M = nb - hh - 2 step) and,
+      // for its wrapped values, 16 lower
       #pragma unroll
       for (int nb = 0; nb < 4; ++nb)
         #pragma unroll
-        for (int hh = 0; hh < 2; ++hh)
-          #pragma unroll
-          for (int i = 0; i < 4; ++i) ptile[wave][16 * nb + r16][16 * hh + 4 * g + i] = p[hh][nb][i];
-      // the tile is private to this wave: LDS accesses of one wave complete in
-      // issue order, so a wave-scope fence (no work-group barrier: waves of a
-      // group may run different trip counts) orders the writes before the reads
-      __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
-      __builtin_amdgcn_wave_barrier();
-      // slot t (d = dbase + t) of this wave's 320 owns diagonal x = t - 255 + 32*step
-      #pragma unroll
-      for (int qd = 0; qd < 5; ++qd) {
-        const int t = lane + 64 * qd;
-        const int x = t - (kVsWaveKeys - 1) + 32 * step;
-        if (x >= -31 && x <= 63) {
-          float acc = 0.f;
-          const int r0 = max(0, x), r1 = min(64, x + 32);
-          for (int r = r0; r < r1; ++r) acc += ptile[wave][r][r - x];
-          dslot[qd] += acc;
+        for (int hh = 0; hh < 2; ++hh) {
+          const float* v = p[hh][nb];
+          const float main = v[0] + dpp_in_row<kRowShl + 1>(v[1]) + dpp_in_row<kRowShl + 2>(v[2]) +
+                             dpp_in_row<kRowShl + 3>(v[3]);
+          const float wrap = dpp_in_row<kRowShr + 15>(v[1]) + dpp_in_row<kRowShr + 14>(v[2]) +
+                             dpp_in_row<kRowShr + 13>(v[3]);
+          const int M = nb - hh - 2 * step;          // -2*kSteps .. 3
+          dacc[M + 2 * kSteps] += main;
+          dacc[M - 1 + 2 * kSteps] += wrap;
         }
-      }
-      __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
-      __builtin_amdgcn_wave_barrier();
     }
   }
 
@@ -261,9 +283,29 @@ __global__ __launch_bounds__(256) void vs_proxy_kernel(VsParams P) {
       }
     }
   } else {
+    // slot t of the wave's kVsDiagSlots partials is offset
+    // row_base - J0 - (kVsWaveKeys - 1) + t; lane (c, g) holds offset
+    // row_base - J0 + 16 M + c - 4g in dacc[M + 2 kSteps]
+    __shared__ float part[4][kM][64];
+    #pragma unroll
+    for (int i = 0; i < kM; ++i) part[wave][i][lane] = dacc[i];
+    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+    __builtin_amdgcn_wave_barrier();
     float* dp = reinterpret_cast<float*>(P.ws_base + P.ws.dpart) + ((size_t)bh * P.ws.nslots + slot) * kVsDiagSlots;
     #pragma unroll
-    for (int qd = 0; qd < 5; ++qd) dp[lane + 64 * qd] = dslot[qd];
+    for (int qd = 0; qd < kVsDiagSlots / 64; ++qd) {
+      const int t = lane + 64 * qd;
+      float acc = 0.f;
+      #pragma unroll
+      for (int gg = 0; gg < 4; ++gg) {
+        const int v = t - (kVsWaveKeys - 1) + 4 * gg;      // 16 M + c
+        const int M = (v + 16 * 2 * kSteps) / 16 - 2 * kSteps;   // floor(v / 16), v >= -16 * 2 kSteps
+        const int c = v & 15;
+        const int mi = M + 2 * kSteps;
+        if (mi >= 0 && mi < kM) acc += part[wave][mi][c + 16 * gg];
+      }
+      dp[t] = acc;
+    }
   }
 }
 
