@@ -36,9 +36,9 @@ PEAK_HBM_GBS = 8000.0            # MI355X HBM3E
 ATTN_KERNEL = "attn_bf16_d128_kernel"
 ATTN_SOURCES = ["long_context_prefill_amd/csrc/attn_bf16.hip", "long_context_prefill_amd/csrc/common.h",
                 "long_context_prefill_amd/csrc/kernels.h", "include/minf.h"]
-ATTN_TRAFFIC = {"workload": "n128k_h32kv8_d128_bf16_mixed", "sources": "9582a3335d5b529c",
-                "fetch_kib": 23832770.04, "fetch_factor": 1048576 / 524302.29,
-                "write_kib": 2110721.57, "write_factor": 1048576 / 1048576.0}
+ATTN_TRAFFIC = {"workload": "n128k_h32kv8_d128_bf16_mixed", "sources": "fa8596f9defe73e4",
+                "fetch_kib": 24291456.79, "fetch_factor": 1048576 / 524302.5,
+                "write_kib": 2111075.19, "write_factor": 1048576 / 1048576.0}
 
 
 def log(*a):
