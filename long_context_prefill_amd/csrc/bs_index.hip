@@ -20,6 +20,29 @@ namespace minf {
 namespace {
 
 typedef float floatx16 __attribute__((ext_vector_type(16)));
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+
+__device__ __forceinline__ floatx16 mma32(u32x4 a, u32x4 b, const floatx16& c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a), __builtin_bit_cast(bf16x8_t, b), c,
+                                                 0, 0, 0);
+}
+
+// Round to the nearest bf16, ties to even (finite inputs).
+__device__ __forceinline__ uint16_t bf16_rne(float x) {
+  const uint32_t b = __builtin_bit_cast(uint32_t, x);
+  return (uint16_t)((b + 0x7fffu + ((b >> 16) & 1u)) >> 16);
+}
+__device__ __forceinline__ float bf16_f32(uint16_t h) { return __builtin_bit_cast(float, (uint32_t)h << 16); }
+
+// x = t0 + t1 + t2 + e with bf16 terms: each term is the nearest bf16 to
+// what the earlier ones leave (the differences are exact in fp32), so
+// |e| <= 2^-24 |x| up to the spacing of the smallest term.
+__device__ __forceinline__ void split3_bf16(float x, uint16_t (&t)[3]) {
+  t[0] = bf16_rne(x);
+  const float r1 = x - bf16_f32(t[0]);
+  t[1] = bf16_rne(r1);
+  t[2] = bf16_rne(r1 - bf16_f32(t[1]));
+}
 
 struct BsBatch {
   int32_t count;
@@ -39,7 +62,8 @@ __global__ __launch_bounds__(256) void bs_pool_kernel(BsParams P, uint64_t kv_us
   const int y = blockIdx.y;
   const int BHq = P.B * P.Hq;
   const T* src;
-  float* dst;
+  float* dst = nullptr;
+  uint16_t* dst3 = nullptr;
   if (y < BHq) {
     const int h = y % P.Hq;
     if (P.ht.kind[h] != MINF_BSPARSE) return;
@@ -50,7 +74,7 @@ __global__ __launch_bounds__(256) void bs_pool_kernel(BsParams P, uint64_t kv_us
     const int kv = z % P.Hkv;
     if (!((kv_used >> kv) & 1ull)) return;
     src = reinterpret_cast<const T*>(P.K) + (size_t)z * P.n * DH;
-    dst = P.kbar + ((size_t)z * P.nq + u) * DH;
+    dst3 = P.kbar3 + ((size_t)z * P.nq + u) * 3 * DH;
   }
   const int r0 = 64 * u, r1 = min(r0 + 64, P.n);
   const int c = threadIdx.x % CPR, rg = threadIdx.x / CPR;
@@ -80,7 +104,15 @@ __global__ __launch_bounds__(256) void bs_pool_kernel(BsParams P, uint64_t kv_us
   if ((int)threadIdx.x < DH) {
     float sum = 0.f;
     for (int g = 0; g < RG; ++g) sum += part[g][threadIdx.x];
-    dst[threadIdx.x] = sum / (float)(r1 - r0);
+    const float mean = sum / (float)(r1 - r0);
+    if (dst) {
+      dst[threadIdx.x] = mean;
+    } else {
+      uint16_t t3[3];
+      split3_bf16(mean, t3);
+      #pragma unroll
+      for (int p = 0; p < 3; ++p) dst3[p * DH + threadIdx.x] = t3[p];
+    }
   }
 }
 
@@ -98,39 +130,41 @@ __device__ __forceinline__ void copy_piece(const float* base, uint32_t voff, uin
       : "memory", "m0");
 }
 
-// grid (items per tile, tiles, batch): causal scores R = scale * Qbar Kbar^T on
-// the fp32 matrix cores (v_mfma_f32_32x32x2_f32).  A work-group holds the 128
-// query blocks of one tile, wave w the 32 blocks U = 4 tile + w, whose pooled
-// rows stay in registers for the whole item (the contraction is only dh
-// long, so operands, not products, are the cost to hide); it sweeps pairs of
-// 32-block column groups (V0, V0 + 1) from the item's first pair to its last,
-// each pair's 64 pooled key rows copied once into LDS for the four waves,
-// double-buffered: the next pair's copies are issued before the current
-// products.  A tile's pairs are split into items of at most `S` pairs,
-// heaviest tiles first, so the grid stays balanced.  Lane (m, hh) of a product
-// holds element k of row m, and the contraction index is permuted alike for
-// both operands, k = k0 + 4 hh + s at step s of the 8-wide slab k0, so one
-// 16-byte read per row and lane feeds four steps; each score is one chain of
-// products in ascending slab order.  LDS rows are stored in 16-byte pieces
-// at position piece ^ (row & 7), so the eight lanes of one LDS read phase hit
-// different banks.
+// grid (items per tile, tiles, batch): causal scores R = scale * Qbar Kbar^T.
+// The products run on the bf16 matrix cores (v_mfma_f32_32x32x16_bf16) with
+// every fp32 operand split into three bf16 terms (hi, mid, lo; the key rows
+// come split from the pooling pass): a . b is summed as hi.hi + (hi.mid +
+// mid.hi) + (hi.lo + mid.mid + lo.hi), whose dropped terms and splitting
+// residue are below 2^-22 of |a| |b| per element, fp32-level error at a
+// sixth of the fp32 matrix instruction's time.  A work-group holds the 128
+// query blocks of one tile, wave w the 32 blocks U = 4 tile + w, whose three
+// terms stay in registers for the whole item; it sweeps the causal key
+// blocks V = 0 .. 4 tile + 3 in steps of 32, each step's 32 split key rows
+// copied once into LDS for the four waves, double-buffered: the next step's
+// copies are issued before the current products.  A tile's steps are split
+// into items of at most `S` steps, heaviest tiles first.  Lane (m, hh) of a
+// product holds elements 16 s + 8 hh .. + 7 of row m at slab s.  LDS rows
+// keep each term's 16-byte pieces at position piece ^ (row & (pieces - 1)),
+// so the lanes of one LDS read phase hit different banks.
 //
 // One counter tracks both loads and stores, in issue order.  Every step
-// issues exactly 32 score stores per wave after its copies (buffer stores:
+// issues exactly 16 score stores per wave after its copies (buffer stores:
 // a score outside the causal triangle or past nq gets an offset beyond the
 // buffer's end and is dropped, so no store depends on a branch), and the
-// wait before the step's barrier leaves those 32 in flight: the copies have
+// wait before the step's barrier leaves those 16 in flight: the copies have
 // landed, the stores keep draining under the next step's products.
 template <int DH>
 __global__ __launch_bounds__(256) void bs_score_kernel(BsParams P, BsBatch batch, int S, int ntiles) {
-  constexpr int CH = DH / 4;       // 16-byte pieces per row
-  constexpr int NG = DH / 8;       // 8-wide slabs
-  constexpr int NI = 64 * CH / 256;   // copies per lane and pair
+  constexpr int NS = DH / 16;         // 16-wide slabs
+  constexpr int PC = DH / 8;          // 16-byte pieces per term of a row
+  constexpr int RP = 3 * PC;          // pieces per staged row
+  constexpr int NI = 32 * RP / 256;   // copies per lane and step
+  static_assert(32 * RP % 256 == 0, "whole copies");
   const int T = ntiles - 1 - (int)blockIdx.y;
-  const int npairs = 2 * T + 2;
+  const int nsteps = 4 * T + 4;
   const int j0 = (int)blockIdx.x * S;
-  if (j0 >= npairs) return;
-  const int j1 = min(j0 + S, npairs);
+  if (j0 >= nsteps) return;
+  const int j1 = min(j0 + S, nsteps);
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: the buffer resource below is scalar
   const int m = lane & 31, hh = lane >> 5;
@@ -140,33 +174,45 @@ __global__ __launch_bounds__(256) void bs_score_kernel(BsParams P, BsBatch batch
   const int kv = h / (P.Hq / P.Hkv);
   const int nq = P.nq;
   const float* A = P.qbar + (size_t)bh * nq * DH;
-  const float* Bm = P.kbar + ((size_t)b * P.Hkv + kv) * nq * DH;
-  __shared__ floatx4 sb[2][64 * CH];
+  const uint16_t* B3 = P.kbar3 + ((size_t)b * P.Hkv + kv) * nq * 3 * DH;
+  __shared__ u32x4 sb[2][32 * RP];
   const uint32_t sbase = (uint32_t)(uintptr_t)&sb[0][0];
 
-  // the copies of pair j into buffer buf: copy i of wave w fills pieces
-  // 256 i + 64 w + lane, i.e. row r = piece / CH at position piece % CH,
-  // which holds the row's piece (position ^ (r & 7))
-  auto copy_pair = [&](int j, int buf) {
+  // the copies of key block V into buffer buf: copy i of wave w fills pieces
+  // 256 i + 64 w + lane, i.e. row r = piece / RP, term q / PC at position
+  // q % PC (q = piece % RP), which holds that term's piece
+  // (position ^ (r & (PC - 1)))
+  auto copy_block = [&](int V, int buf) {
     #pragma unroll
     for (int i = 0; i < NI; ++i) {
       const int pos = 256 * i + 64 * wave + lane;
-      const int r = pos / CH;
-      const int c = (pos % CH) ^ (r & 7);
-      const int row = min(64 * j + r, nq - 1);     // rows past nq: computed, never stored
-      const uint32_t dst = __builtin_amdgcn_readfirstlane(sbase + (uint32_t)(buf * 64 * CH + 256 * i + 64 * wave) * 16);
-      copy_piece(Bm, (uint32_t)((row * DH + 4 * c) * 4), dst);
+      const int r = pos / RP, q = pos % RP;
+      const int term = q / PC, c = (q % PC) ^ (r & (PC - 1));
+      const int row = min(32 * V + r, nq - 1);     // rows past nq: computed, never stored
+      const uint32_t dst = __builtin_amdgcn_readfirstlane(sbase + (uint32_t)(buf * 32 * RP + 256 * i + 64 * wave) * 16);
+      copy_piece(reinterpret_cast<const float*>(B3), (uint32_t)(((row * 3 + term) * DH + 8 * c) * 2), dst);
     }
   };
-  copy_pair(j0, 0);
-  floatx4 a[NG];
+  copy_block(j0, 0);
+  // this wave's pooled query rows as three bf16 terms
+  u32x4 a[3][NS];
   {
-    const float* pa = A + (size_t)min(32 * U + m, nq - 1) * DH + 4 * hh;
+    const float* pa = A + (size_t)min(32 * U + m, nq - 1) * DH + 8 * hh;
     #pragma unroll
-    for (int g = 0; g < NG; ++g) a[g] = *reinterpret_cast<const floatx4*>(pa + 8 * g);
+    for (int sl = 0; sl < NS; ++sl) {
+      const floatx4 x0 = *reinterpret_cast<const floatx4*>(pa + 16 * sl);
+      const floatx4 x1 = *reinterpret_cast<const floatx4*>(pa + 16 * sl + 4);
+      uint16_t t[8][3];
+      #pragma unroll
+      for (int e = 0; e < 4; ++e) { split3_bf16(x0[e], t[e]); split3_bf16(x1[e], t[4 + e]); }
+      #pragma unroll
+      for (int q = 0; q < 3; ++q)
+        #pragma unroll
+        for (int e = 0; e < 4; ++e) a[q][sl][e] = (uint32_t)t[2 * e][q] | ((uint32_t)t[2 * e + 1][q] << 16);
+    }
   }
   // everything above has landed (a real wait instruction, so that the
-  // compiler knows the query rows need no wait inside the sweep)
+  // compiler knows the query terms need no wait inside the sweep)
   __builtin_amdgcn_s_waitcnt(0x0f70);    // vmcnt(0)
   __syncthreads();
 
@@ -176,50 +222,40 @@ __global__ __launch_bounds__(256) void bs_score_kernel(BsParams P, BsBatch batch
   const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
       P.scores + ((size_t)blockIdx.z * nq + (size_t)32 * U) * nq, 0, (int)rows_bytes, 0x00020000);
   const float scale = P.scale;
-  auto store_block = [&](const floatx16& acc, int V) {
-    // lane (m, hh), register r of a 32x32 product: row 8 (r / 4) + 4 hh + r % 4, column m
+  for (int j = j0; j < j1; ++j) {
+    const int buf = (j - j0) & 1;
+    const int V = j;
+    // the other buffer was read in the previous step, before its barrier
+    if (j + 1 < j1) copy_block(j + 1, buf ^ 1);
+    floatx16 c0, c1, c2;
+    #pragma unroll
+    for (int r = 0; r < 16; ++r) { c0[r] = 0.f; c1[r] = 0.f; c2[r] = 0.f; }
+    if (V <= U) {
+      const u32x4* srow = &sb[buf][m * RP];
+      #pragma unroll
+      for (int sl = 0; sl < NS; ++sl) {
+        const int c = (2 * sl + hh) ^ (m & (PC - 1));
+        const u32x4 b0 = srow[c], b1 = srow[PC + c], b2 = srow[2 * PC + c];
+        c0 = mma32(a[0][sl], b0, c0);
+        c1 = mma32(a[0][sl], b1, c1);
+        c2 = mma32(a[0][sl], b2, c2);
+        c1 = mma32(a[1][sl], b0, c1);
+        c2 = mma32(a[1][sl], b1, c2);
+        c2 = mma32(a[2][sl], b0, c2);
+      }
+    }
+    // lane (m, hh), register r of a 32x32 product: row 8 (r / 4) + 4 hh + r % 4,
+    // column m; a block past U (the diagonal) stores nothing
     const int vv = 32 * V + m;
     #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const int ul = 8 * (r >> 2) + 4 * hh + (r & 3);
       const int uu = 32 * U + ul;
       const uint32_t off = (uu < nq && vv <= uu) ? (uint32_t)((ul * nq + vv) * 4) : 0x7ffffff0u;
-      __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, scale * acc[r]), rsrc, (int)off, 0, 0);
+      const float x = scale * (c0[r] + (c1[r] + c2[r]));
+      __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, x), rsrc, (int)off, 0, 0);
     }
-  };
-  for (int j = j0; j < j1; ++j) {
-    const int buf = (j - j0) & 1;
-    const int V0 = 2 * j;
-    // the other buffer was read in the previous step, before its barrier
-    if (j + 1 < j1) copy_pair(j + 1, buf ^ 1);
-    const floatx4* s0 = &sb[buf][m * CH];
-    const floatx4* s1 = &sb[buf][(32 + m) * CH];
-    floatx16 acc0, acc1;
-    #pragma unroll
-    for (int r = 0; r < 16; ++r) { acc0[r] = 0.f; acc1[r] = 0.f; }
-    if (V0 + 1 <= U) {
-      #pragma unroll
-      for (int g = 0; g < NG; ++g) {
-        const floatx4 b0 = s0[(2 * g + hh) ^ (m & 7)];
-        const floatx4 b1 = s1[(2 * g + hh) ^ (m & 7)];
-        #pragma unroll
-        for (int st = 0; st < 4; ++st) {
-          acc0 = __builtin_amdgcn_mfma_f32_32x32x2f32(a[g][st], b0[st], acc0, 0, 0, 0);
-          acc1 = __builtin_amdgcn_mfma_f32_32x32x2f32(a[g][st], b1[st], acc1, 0, 0, 0);
-        }
-      }
-    } else if (V0 <= U) {
-      #pragma unroll
-      for (int g = 0; g < NG; ++g) {
-        const floatx4 b0 = s0[(2 * g + hh) ^ (m & 7)];
-        #pragma unroll
-        for (int st = 0; st < 4; ++st) acc0 = __builtin_amdgcn_mfma_f32_32x32x2f32(a[g][st], b0[st], acc0, 0, 0, 0);
-      }
-    }
-    // blocks past U (the diagonal pair) store nothing: every offset is out of range
-    store_block(acc0, V0);
-    store_block(acc1, V0 + 1);
-    asm volatile("s_waitcnt vmcnt(32)\n\ts_barrier" ::: "memory");
+    asm volatile("s_waitcnt vmcnt(16)\n\ts_barrier" ::: "memory");
   }
 }
 
@@ -286,15 +322,15 @@ hipError_t launch_t(const BsParams& p, hipStream_t st) {
   const int tiles = (p.nq + 127) / 128;
   auto flush = [&]() {
     if (!batch.count) return;
-    // pairs per score item: the longest that still gives about three items
-    // per resident work-group slot (two per CU)
-    int S = 4;
-    for (int cand : {16, 8}) {
+    // key blocks per score item: the longest that still gives about three
+    // items per resident work-group slot (two per CU)
+    int S = 8;
+    for (int cand : {32, 16}) {
       int64_t items = 0;
-      for (int t = 0; t < tiles; ++t) items += (2 * t + 2 + cand - 1) / cand;
+      for (int t = 0; t < tiles; ++t) items += (4 * t + 4 + cand - 1) / cand;
       if (items * batch.count >= 3 * 512) { S = cand; break; }
     }
-    const int per_tile = (2 * tiles + S - 1) / S;
+    const int per_tile = (4 * tiles + S - 1) / S;
     hipLaunchKernelGGL((bs_score_kernel<DH>), dim3(per_tile, tiles, batch.count), dim3(256), 0, st, p, batch, S, tiles);
     const int64_t per = (p.nq + 255) / 256;   // scores per thread
     if (per <= 4) launch_topk<4>(p, batch, st);

@@ -142,7 +142,7 @@ BsWs bs_ws(const minf_problem* p, const Derived& d) {
   Carve c;
   BsWs w;
   w.qbar = c.take((size_t)p->B * p->Hq * d.nq * p->dh * 4);
-  w.kbar = c.take((size_t)p->B * p->Hkv * d.nq * p->dh * 4);
+  w.kbar = c.take((size_t)p->B * p->Hkv * d.nq * p->dh * 3 * 2);
   const size_t per_head = (size_t)d.nq * d.nq * 4;
   const int64_t heads = (int64_t)p->B * std::max(d.hq_bs, 1);
   w.score_heads = std::max<int64_t>(1, std::min<int64_t>({heads, 64, (int64_t)(kScoreBytesCap / per_head)}));
@@ -332,7 +332,7 @@ minf_status minf_bs_index(const minf_problem* prob, const minf_head_cfg* heads, 
   minf::BsParams b{};
   b.Q = Q; b.K = K; b.blk_idx = blk_idx; b.blk_cnt = blk_cnt;
   b.qbar = reinterpret_cast<float*>(static_cast<char*>(ws) + w.qbar);
-  b.kbar = reinterpret_cast<float*>(static_cast<char*>(ws) + w.kbar);
+  b.kbar3 = reinterpret_cast<uint16_t*>(static_cast<char*>(ws) + w.kbar);
   b.scores = reinterpret_cast<float*>(static_cast<char*>(ws) + w.scores);
   b.score_heads = w.score_heads;
   b.max_kb = d.max_kb;

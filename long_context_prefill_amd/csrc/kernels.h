@@ -239,7 +239,7 @@ struct BsParams {
   int32_t* blk_idx;
   int32_t* blk_cnt;
   float* qbar;      // ws [B,Hq,nq,dh]
-  float* kbar;      // ws [B,Hkv,nq,dh]
+  uint16_t* kbar3;  // ws [B,Hkv,nq,3,dh]: each pooled key row as three bf16 terms (hi, mid, lo)
   float* scores;    // ws [heads in batch, nq, nq]
   int64_t score_heads;   // heads whose score matrices fit the workspace at once
   int64_t max_kb;
