@@ -140,9 +140,11 @@ __device__ void block_topk_reg(Get get, int n, int k, int32_t* __restrict__ out,
   }
   for (int i = tid; i < 4 * 256; i += NT) sh.hist[i >> 8][i & 255] = 0;
   __syncthreads();
-  // first digit: every key takes part
+  // first digit: every key takes part, and the keys of a row mostly share
+  // their top byte, so the lanes of the most common bins are counted
+  // together
   #pragma unroll
-  for (int e = 0; e < E; ++e) atomicAdd(&sh.hist[wave][key[e] >> 24], 1);
+  for (int e = 0; e < E; ++e) hist_add(sh.hist[wave], true, key[e] >> 24);
   __syncthreads();
   pick_digit(sh.hist[0][tid] + sh.hist[1][tid] + sh.hist[2][tid] + sh.hist[3][tid], k, 0u, 0u, 24, sh.scan,
              &sh.prefix, &sh.mask, &sh.remaining);
