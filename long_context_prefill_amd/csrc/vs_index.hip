@@ -369,8 +369,19 @@ __device__ __forceinline__ float get_c(const float* p) {
   return __int_as_float(
       __hip_atomic_load(reinterpret_cast<const int*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
 }
-// wait until this wave's memory operations have completed
-__device__ __forceinline__ void drain() { __builtin_amdgcn_s_waitcnt(0); }
+// Wait until this wave's memory operations have completed.  The hand-offs
+// between work-groups rest on two properties of this hardware rather than
+// on release/acquire atomics (which at agent scope write back or invalidate
+// the XCD's whole L2 at every hand-off): a store is visible to every XCD
+// once the issuing wave's counter has drained, because the exchanged values
+// bypass L2; and a wave's loads issue in program order after the flag load
+// that released them.  The compiler fences keep the compiler itself from
+// moving memory accesses across the wait.
+__device__ __forceinline__ void drain() {
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_s_waitcnt(0);
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
 
 // ---------------------------------------------------------------- single-launch proxy
 // The same proxy in one launch (minf_vs_index_fused): pass 1, the LSE fold
@@ -695,6 +706,8 @@ __global__ __launch_bounds__(256) void vs_fused_kernel(VsParams P, VsFusedMeta M
         __builtin_amdgcn_s_sleep(8);
       }
       s_val = ok;
+      // the LSE loads below stay after the flag load
+      __atomic_signal_fence(__ATOMIC_SEQ_CST);
     }
     __syncthreads();
     if (!s_val) {
