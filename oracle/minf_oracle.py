@@ -14,7 +14,7 @@ build_c()).  Sources (cited by page title and section):
 * [Blog]  blog-zz7 "LLM模型之MInference", section 2.3
 * [Cost]  PaperTrace 1.1.1 "成本模型：训练、prefill、解码与 KV cache"
 
-Readings taken where the pages are open (each is listed in the design doc):
+Readings taken where the pages are open:
 
 * slash expansion: a slash offset d covers, for the query block u of
   ``slash_tile`` rows, the keys [t*u - d, t*u + t - 1 - d]  (t = slash_tile;

@@ -10,7 +10,7 @@ Q is [B, Hq, n, dh], K and V are [B, Hkv, n, dh], contiguous.  Half-precision
 tensors are returned as raw bfloat16 bit patterns (numpy uint16), fp32 tensors
 as numpy float32.
 
-Recipe (fixed before any measurement; every constant is listed in the design doc):
+Recipe (fixed before any measurement):
 
 * Workload ``k`` (1..5) is seeded with ``1000 + k``.
   ``SeedSequence(seed).spawn(6)`` gives, in order, the streams for Q, K, V, the
