@@ -152,7 +152,9 @@ __device__ __forceinline__ ItemLists item_lists(const AttnParams& P, const Sampl
 // Work items are (batch, head, query block) triples, handed out through one
 // queue per XCD: the attention kernel runs persistent work-groups (four per
 // CU) and work-group i serves the queue of XCD i mod 8, the XCD the
-// hardware dispatches it to.  Items are grouped into units:
+// hardware dispatches it to; once that queue is empty it takes items from
+// the other queues in turn, so that the XCDs finish together even where
+// their items ran at different speeds.  Items are grouped into units:
 // * a Vertical-Slash or A-shape unit is a run of consecutive query blocks of
 //   one (batch, head) pair (the run length comes from attn_sched_shape); its
 //   blocks are queued from the last to the first;
@@ -971,10 +973,12 @@ __device__ __forceinline__ void attn_item(const AttnParams& P, const SampleView&
 
 __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void attn_bf16_d128_kernel(AttnParams P) {
-  // persistent: take items from this XCD's queue until it is empty
-  const int xcd = blockIdx.x & 7;
-  const int qoff = P.queue_meta[xcd];
-  const int qcnt = P.queue_meta[8 + xcd];
+  // persistent: take items from this XCD's queue until it is empty, then
+  // from the other XCDs' queues in turn until all eight are
+  int xq = blockIdx.x & 7;
+  int hops = 0;
+  int qoff = P.queue_meta[xq];
+  int qcnt = P.queue_meta[8 + xq];
   __shared__ __attribute__((aligned(16))) char smem_g[kSmem];
   lds_char* smem = (lds_char*)smem_g;
   // tickets: the first here, each next one by the item before it (during its
@@ -982,14 +986,26 @@ void attn_bf16_d128_kernel(AttnParams P) {
   // barriers between items wait for LDS only: the output stores complete
   // while the next item loads its lists.
   int* s_tk = reinterpret_cast<int*>(smem_g + kTicket);
-  int* tkp = &P.queue_meta[16 + xcd];
+  int* tkp = &P.queue_meta[16 + xq];
   if (threadIdx.x == 0) *s_tk = atomicAdd(tkp, 1);
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
   while (true) {
     const int qi = __builtin_amdgcn_readfirstlane(*s_tk);
     // both waves hold qi before the ticket word is written again
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-    if (qi >= qcnt) break;
+    if (qi >= qcnt) {
+      // this queue is drained: the work-group helps with the next XCD's
+      // queue (its items run from keys cached in another L2, but only while
+      // the queues run out, when the XCDs would otherwise finish unevenly)
+      if (++hops == 8) break;
+      xq = __builtin_amdgcn_readfirstlane((xq + 1) & 7);
+      qoff = __builtin_amdgcn_readfirstlane(P.queue_meta[xq]);
+      qcnt = __builtin_amdgcn_readfirstlane(P.queue_meta[8 + xq]);
+      tkp = &P.queue_meta[16 + xq];
+      if (threadIdx.x == 0) *s_tk = atomicAdd(tkp, 1);
+      asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+      continue;
+    }
     const int item = ld_uniform(P.queue, (int64_t)qoff + qi);
     const int bhi = item / P.nq;
     const int u = item % P.nq;
