@@ -36,9 +36,9 @@ PEAK_HBM_GBS = 8000.0            # MI355X HBM3E
 ATTN_KERNEL = "attn_bf16_d128_kernel"
 ATTN_SOURCES = ["long_context_prefill_amd/csrc/attn_bf16.hip", "long_context_prefill_amd/csrc/common.h",
                 "long_context_prefill_amd/csrc/kernels.h", "include/minf.h"]
-ATTN_TRAFFIC = {"workload": "n128k_h32kv8_d128_bf16_mixed", "sources": "a03f445fe68d38a5",
-                "fetch_kib": 24197837.0, "fetch_factor": 1048576 / 524302.6,
-                "write_kib": 2111062.47, "write_factor": 1048576 / 1048576.0}
+ATTN_TRAFFIC = {"workload": "n128k_h32kv8_d128_bf16_mixed", "sources": "39f0fe2b5db47586",
+                "fetch_kib": 24482496.42, "fetch_factor": 1048576 / 524302.4,
+                "write_kib": 2112749.89, "write_factor": 1048576 / 1048576.0}
 
 
 def log(*a):
