@@ -12,6 +12,8 @@
 // batch of heads into the workspace (so the score matrix never has to be
 // resident for the whole layer); one work-group per (head, query block) then
 // runs the exact radix top-k on its row.
+#include <type_traits>
+
 #include "kernels.h"
 #include "topk.h"
 
@@ -266,9 +268,83 @@ __global__ __launch_bounds__(256) void bs_score_kernel(BsParams P, BsBatch batch
 // one load instruction of a wave would touch 64 cache lines, so the row is
 // first copied into LDS with consecutive lanes on consecutive scores (one
 // padding word per 32 keeps the per-thread reads free of bank conflicts).
-template <int E>
-__global__ __launch_bounds__(256) void bs_topk_kernel(BsParams P, BsBatch batch) {
-  const int u = blockIdx.x;
+// Top-k of a row staged in LDS (srow, W words), E2 scores per thread.  When
+// k is small against n, a sample of the row (each thread's first score)
+// bounds the candidates first: Ts is the r-th largest sample, with r about
+// three standard deviations above the number of samples expected above the
+// k-th largest score.  If at least k scores are >= Ts (then every score >=
+// the k-th largest is among them) and they fit, they are copied in index
+// order over the staged row and the exact selection runs on them alone (ties
+// still go to the lowest index: the copy keeps the order); otherwise it runs
+// on the whole row.  Either way the result is the exact top-k.
+template <int E2, int W, bool SAMPLE, typename Get>
+__device__ void row_topk(Get get, int n, int k, int32_t* __restrict__ out, int cap, TopkRegShared& sh,
+                         float* srow) {
+  // candidate (key, index) pairs that fit: 1024 or 2048 (E2 >= 8 gives W >=
+  // 2112 words)
+  constexpr int PAIRS = W / 2 >= 2048 ? 2048 : 1024;
+  k = min(k, n);
+  auto ident = [](int i) { return i; };
+  if (topk_trivial<256>(ident, n, k, out, cap)) return;
+  uint32_t key[E2];
+  load_keys<E2>(get, n, key);
+  // threads past the row contribute key 0, below every real key; r <= ns
+  // keeps the threshold a real key, so no slot past n is a candidate
+  const int lo = (int)threadIdx.x * E2;
+  uint32_t ts = 0;
+  int total = 0, pos = 0;
+  if (SAMPLE && 4 * k <= n) {
+    const int ns = (n + E2 - 1) / E2;
+    const float m = (float)k * (float)ns / (float)n;
+    const int r = min(ns, (int)(m + 3.0f * __builtin_sqrtf(m)) + 3);
+    ts = block_kth_key(key[0], r, sh);
+    int nc = 0;
+    #pragma unroll
+    for (int e = 0; e < E2; ++e) nc += key[e] >= ts;
+    pos = block_scan_excl<256>(nc, sh.scan, &total);
+  }
+  if (total < k || total > PAIRS) {
+    topk_keys<256, E2>(key, ident, k, out, cap, sh);
+    return;
+  }
+  // every thread has read its scores (the barriers above): the row's LDS
+  // now holds the candidates' keys, then their indices
+  uint32_t* ck = reinterpret_cast<uint32_t*>(srow);
+  int32_t* ci = reinterpret_cast<int32_t*>(srow) + PAIRS;
+  #pragma unroll
+  for (int e = 0; e < E2; ++e)
+    if (key[e] >= ts) {
+      ck[pos] = key[e];
+      ci[pos] = lo + e;
+      ++pos;
+    }
+  __syncthreads();
+  auto idxc = [&](int i) { return ci[i]; };
+  // candidate slots CE t .. CE t + CE - 1 of thread t (below PAIRS); slots
+  // past total get key 0
+  auto run = [&](auto ce) {
+    constexpr int CE = decltype(ce)::value;
+    uint32_t kc[CE];
+    #pragma unroll
+    for (int e = 0; e < CE; ++e) {
+      const int i = (int)threadIdx.x * CE + e;
+      kc[e] = i < total ? ck[i] : 0u;
+    }
+    topk_keys<256, CE>(kc, idxc, k, out, cap, sh);
+  };
+  if (total <= 512) run(std::integral_constant<int, 2>{});
+  else if (total <= 1024) run(std::integral_constant<int, 4>{});
+  else run(std::integral_constant<int, PAIRS / 256>{});
+}
+
+// Rows u0 .. u0 + gridDim.x - 1 of the batch's heads, each at most 256 E
+// scores, held E per thread (E_LO for rows of at most 256 E_LO); SAMPLE
+// bounds the candidates by a sample first (row_topk).  One launch per
+// row-length range, so that every launch stages its rows in an LDS row of
+// about their size.
+template <int E, int E_LO, bool SAMPLE>
+__global__ __launch_bounds__(256) void bs_topk_kernel(BsParams P, BsBatch batch, int u0) {
+  const int u = u0 + (int)blockIdx.x;
   const int bh = batch.bh[blockIdx.y];
   const int h = bh % P.Hq;
   __shared__ TopkRegShared sh;
@@ -301,15 +377,31 @@ __global__ __launch_bounds__(256) void bs_topk_kernel(BsParams P, BsBatch batch)
     const bool forced = ((force & MINF_FORCE_FIRST_BLOCK) && v == 0) || ((force & MINF_FORCE_DIAG_BLOCK) && v == u);
     return forced ? __builtin_huge_valf() : x;
   };
-  if (E >= 16 && n <= 64 * E) block_topk_reg<256, (E >= 16 ? E / 4 : E)>(get, n, k, out, (int)P.max_kb, sh);
-  else if (E >= 8 && n <= 128 * E) block_topk_reg<256, (E >= 8 ? E / 2 : E)>(get, n, k, out, (int)P.max_kb, sh);
-  else block_topk_reg<256, E>(get, n, k, out, (int)P.max_kb, sh);
+  constexpr int W = E * 256 + E * 8;
+  if (E_LO < E && n <= 256 * E_LO) row_topk<E_LO, W, false>(get, n, k, out, (int)P.max_kb, sh, srow);
+  else row_topk<E, W, SAMPLE>(get, n, k, out, (int)P.max_kb, sh, srow);
   if (threadIdx.x == 0) P.blk_cnt[(size_t)bh * P.nq + u] = k;
 }
 
-template <int E>
+// Rows of up to 1024 scores take four per thread, up to 2048 eight (one
+// launch); then each doubling of the row length doubles the width, up to 128
+// (32768 blocks, the most a Block-Sparse row may hold).  Rows of 2048 to
+// 8191 scores bound their candidates by a sample first (the 512K layer's
+// Block-Sparse index went from 7.3 to 6.3 ms); on rows of 1024 to 2047 that
+// was 10% slower (the radix passes over eight registers cost less than the
+// extra passes over the sample), and the widest rows keep the plain path,
+// whose registers the sampling would overflow.
 static void launch_topk(const BsParams& p, const BsBatch& batch, hipStream_t st) {
-  hipLaunchKernelGGL(bs_topk_kernel<E>, dim3(p.nq, batch.count), dim3(256), 0, st, p, batch);
+  for (int64_t lo = 0; lo < p.nq; lo = lo ? 2 * lo : 2048) {
+    const int64_t hi = std::min<int64_t>(lo ? 2 * lo : 2048, p.nq);
+    const dim3 grid((unsigned)(hi - lo), batch.count);
+    const int u0 = (int)lo;
+    if (hi <= 2048) hipLaunchKernelGGL((bs_topk_kernel<8, 4, false>), grid, dim3(256), 0, st, p, batch, u0);
+    else if (hi <= 4096) hipLaunchKernelGGL((bs_topk_kernel<16, 16, true>), grid, dim3(256), 0, st, p, batch, u0);
+    else if (hi <= 8192) hipLaunchKernelGGL((bs_topk_kernel<32, 32, true>), grid, dim3(256), 0, st, p, batch, u0);
+    else if (hi <= 16384) hipLaunchKernelGGL((bs_topk_kernel<64, 64, false>), grid, dim3(256), 0, st, p, batch, u0);
+    else hipLaunchKernelGGL((bs_topk_kernel<128, 128, false>), grid, dim3(256), 0, st, p, batch, u0);
+  }
 }
 
 template <typename T, int DH>
@@ -332,13 +424,7 @@ hipError_t launch_t(const BsParams& p, hipStream_t st) {
     }
     const int per_tile = (4 * tiles + S - 1) / S;
     hipLaunchKernelGGL((bs_score_kernel<DH>), dim3(per_tile, tiles, batch.count), dim3(256), 0, st, p, batch, S, tiles);
-    const int64_t per = (p.nq + 255) / 256;   // scores per thread
-    if (per <= 4) launch_topk<4>(p, batch, st);
-    else if (per <= 8) launch_topk<8>(p, batch, st);
-    else if (per <= 16) launch_topk<16>(p, batch, st);
-    else if (per <= 32) launch_topk<32>(p, batch, st);
-    else if (per <= 64) launch_topk<64>(p, batch, st);
-    else launch_topk<128>(p, batch, st);
+    launch_topk(p, batch, st);
     batch.count = 0;
   };
   const int cap = (int)std::min<int64_t>(p.score_heads, 64);

@@ -95,9 +95,10 @@ __device__ __forceinline__ void hist_add(int* hist, bool act, uint32_t bin) {
   if (act) atomicAdd(&hist[bin], 1);
 }
 
-// Selects the top min(k, n) of get(0..n-1), up to NT * E elements held in
-// registers, and writes their indices, ascending, to out[0..); out[min(k,n)
-// .. cap) is filled with -1.  Thread t reads elements [t*E, t*E + E) once;
+// block_topk_reg selects the top min(k, n) of get(0..n-1), up to NT * E
+// elements held in registers, and writes idx of their positions, ascending,
+// to out[0..); out[min(k,n) .. cap) is filled with -1 (idx is the identity
+// unless given).  Thread t reads elements [t*E, t*E + E) once;
 // the four radix passes and the ordered compaction work on those registers.
 // `get(i)` is called once for every i < NT * E (also past n, where its value
 // is discarded), must be safe to call there and must not return NaN.  Slots past
@@ -113,31 +114,16 @@ struct TopkRegShared {
   int remaining;
 };
 
-template <int NT, int E, typename Get>
-__device__ void block_topk_reg(Get get, int n, int k, int32_t* __restrict__ out, int cap, TopkRegShared& sh) {
-  static_assert(NT == 256, "block_topk_reg: 256 threads");
+// The selection itself on keys already in registers: thread t holds the
+// keys of elements lo .. lo + E - 1 (lo = t * E), key 0 for slots past n, and
+// 0 < k < n.  The indices written are idx(element).
+template <int NT, int E, typename Idx>
+__device__ void topk_keys(const uint32_t (&key)[E], Idx idx, int k, int32_t* __restrict__ out, int cap,
+                          TopkRegShared& sh) {
+  static_assert(NT == 256, "topk_keys: 256 threads");
   const int tid = threadIdx.x;
   const int wave = tid >> 6;
-  k = min(k, n);
   const int lo = tid * E;
-  if (k <= 0) {
-    for (int i = tid; i < cap; i += NT) out[i] = -1;
-    __syncthreads();
-    return;
-  }
-  if (k >= n) {
-    // every element is taken
-    for (int i = tid; i < n; i += NT) out[i] = i;
-    for (int i = n + tid; i < cap; i += NT) out[i] = -1;
-    __syncthreads();
-    return;
-  }
-  uint32_t key[E];
-  #pragma unroll
-  for (int e = 0; e < E; ++e) {
-    const uint32_t x = order_key(get(lo + e));
-    key[e] = lo + e < n ? x : 0u;
-  }
   for (int i = tid; i < 4 * 256; i += NT) sh.hist[i >> 8][i & 255] = 0;
   __syncthreads();
   // first digit: every key takes part, and the keys of a row mostly share
@@ -178,10 +164,84 @@ __device__ void block_topk_reg(Get get, int n, int k, int32_t* __restrict__ out,
   for (int e = 0; e < E; ++e) {
     bool sel = key[e] > T;
     if (!sel && key[e] == T) { sel = eq_seen < take_eq; ++eq_seen; }
-    if (sel) out[pos++] = lo + e;
+    if (sel) out[pos++] = idx(lo + e);
   }
   for (int i = k + tid; i < cap; i += NT) out[i] = -1;
   __syncthreads();
+}
+
+// Outputs of the cases without a selection: k <= 0 (none taken) or k >= n
+// (all taken).  Returns false when a selection is needed.
+template <int NT, typename Idx>
+__device__ bool topk_trivial(Idx idx, int n, int k, int32_t* __restrict__ out, int cap) {
+  const int tid = threadIdx.x;
+  if (k <= 0) {
+    for (int i = tid; i < cap; i += NT) out[i] = -1;
+    __syncthreads();
+    return true;
+  }
+  if (k >= n) {
+    for (int i = tid; i < n; i += NT) out[i] = idx(i);
+    for (int i = n + tid; i < cap; i += NT) out[i] = -1;
+    __syncthreads();
+    return true;
+  }
+  return false;
+}
+
+// Loads the keys of get(lo .. lo + E - 1) (key 0 past n).
+template <int E, typename Get>
+__device__ __forceinline__ void load_keys(Get get, int n, uint32_t (&key)[E]) {
+  const int lo = (int)threadIdx.x * E;
+  #pragma unroll
+  for (int e = 0; e < E; ++e) {
+    const uint32_t x = order_key(get(lo + e));
+    key[e] = lo + e < n ? x : 0u;
+  }
+}
+
+template <int NT, int E, typename Get, typename Idx>
+__device__ void block_topk_reg(Get get, Idx idx, int n, int k, int32_t* __restrict__ out, int cap,
+                               TopkRegShared& sh) {
+  k = min(k, n);
+  if (topk_trivial<NT>(idx, n, k, out, cap)) return;
+  uint32_t key[E];
+  load_keys<E>(get, n, key);
+  topk_keys<NT, E>(key, idx, k, out, cap, sh);
+}
+template <int NT, int E, typename Get>
+__device__ void block_topk_reg(Get get, int n, int k, int32_t* __restrict__ out, int cap, TopkRegShared& sh) {
+  block_topk_reg<NT, E>(get, [](int i) { return i; }, n, k, out, cap, sh);
+}
+
+// The float whose order_key is key (order_key is a bijection on bit patterns).
+__device__ __forceinline__ float key_float(uint32_t key) {
+  return __builtin_bit_cast(float, (key & 0x80000000u) ? (key & 0x7fffffffu) : ~key);
+}
+
+// The r-th largest (1 <= r <= 256) of the 256 keys x, one per thread, by the
+// same four radix passes.
+__device__ __forceinline__ uint32_t block_kth_key(uint32_t x, int r, TopkRegShared& sh) {
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6;
+  for (int i = tid; i < 4 * 256; i += 256) sh.hist[i >> 8][i & 255] = 0;
+  __syncthreads();
+  hist_add(sh.hist[wave], true, x >> 24);
+  __syncthreads();
+  pick_digit(sh.hist[0][tid] + sh.hist[1][tid] + sh.hist[2][tid] + sh.hist[3][tid], r, 0u, 0u, 24, sh.scan,
+             &sh.prefix, &sh.mask, &sh.remaining);
+  for (int shift = 16; shift >= 0; shift -= 8) {
+    for (int i = tid; i < 4 * 256; i += 256) sh.hist[i >> 8][i & 255] = 0;
+    __syncthreads();
+    const uint32_t prefix = sh.prefix, mask = sh.mask;
+    const int rem = sh.remaining;
+    const bool mt = (x & mask) == prefix;
+    if (__ballot(mt) != 0ull && mt) atomicAdd(&sh.hist[wave][(x >> shift) & 255u], 1);
+    __syncthreads();
+    const int tot = sh.hist[0][tid] + sh.hist[1][tid] + sh.hist[2][tid] + sh.hist[3][tid];
+    pick_digit(tot, rem, prefix, mask, shift, sh.scan, &sh.prefix, &sh.mask, &sh.remaining);
+  }
+  return sh.prefix;
 }
 
 }  // namespace minf
