@@ -37,8 +37,8 @@ ATTN_KERNEL = "attn_bf16_d128_kernel"
 ATTN_SOURCES = ["long_context_prefill_amd/csrc/attn_bf16.hip", "long_context_prefill_amd/csrc/common.h",
                 "long_context_prefill_amd/csrc/kernels.h", "include/minf.h"]
 ATTN_TRAFFIC = {"workload": "n128k_h32kv8_d128_bf16_mixed", "sources": "39f0fe2b5db47586",
-                "fetch_kib": 24482496.42, "fetch_factor": 1048576 / 524302.4,
-                "write_kib": 2112749.89, "write_factor": 1048576 / 1048576.0}
+                "fetch_kib": 24166308.27, "fetch_factor": 1048576 / 524303.6,
+                "write_kib": 2112675.11, "write_factor": 1048576 / 1048576.0}
 
 
 def log(*a):
