@@ -36,7 +36,7 @@ PEAK_HBM_GBS = 8000.0            # MI355X HBM3E
 ATTN_KERNEL = "attn_bf16_d128_kernel"
 ATTN_SOURCES = ["long_context_prefill_amd/csrc/attn_bf16.hip", "long_context_prefill_amd/csrc/common.h",
                 "long_context_prefill_amd/csrc/kernels.h", "include/minf.h"]
-ATTN_TRAFFIC = {"workload": "n128k_h32kv8_d128_bf16_mixed", "sources": "39f0fe2b5db47586",
+ATTN_TRAFFIC = {"workload": "n128k_h32kv8_d128_bf16_mixed", "sources": "84f88fa25b3e4d54",
                 "fetch_kib": 24166308.27, "fetch_factor": 1048576 / 524303.6,
                 "write_kib": 2112675.11, "write_factor": 1048576 / 1048576.0}
 
@@ -445,7 +445,7 @@ def main():
                     help="only run a plain device copy of this many MiB (memory-counter calibration)")
     a = ap.parse_args()
     if a.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py runs on one GPU only: this build has no multi-GPU path "
+        print("bench.py runs on one GPU only: the library has no multi-GPU path "
               "(sharding over KV-head groups is a design note, not code).", file=sys.stderr)
         sys.exit(2)
 

@@ -49,7 +49,7 @@ extern "C" {
 typedef enum {
   MINF_OK = 0,
   MINF_EINVAL = 1,         /* malformed shapes, pointers or head table          */
-  MINF_EUNSUPPORTED = 2,   /* valid request this build does not implement      */
+  MINF_EUNSUPPORTED = 2,   /* valid request the library does not implement     */
   MINF_EWORKSPACE = 3,     /* workspace smaller than minf_query_sizes() asks    */
   MINF_ECAPACITY = 4,      /* an output buffer capacity is too small            */
   MINF_EHIP = 5            /* a HIP launch failed                               */
