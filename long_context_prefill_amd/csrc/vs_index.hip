@@ -15,10 +15,13 @@
 //  lse     the partials of each row are combined in a fixed order;
 //  pass 2  the same S^T tiles are recomputed and turned into exact
 //          probabilities; column sums are finished inside the wave (every key
-//          belongs to exactly one wave) and diagonal sums are accumulated per
-//          wave through a small LDS tile, then written as partials;
+//          belongs to exactly one wave) and diagonal sums are accumulated in
+//          registers (lane shifts within 16-lane rows), combined per wave
+//          through LDS and written as partials;
 //  diag    each offset's two neighbouring partials are added in a fixed order;
-//  top-k   exact radix select per (head, score array).
+//  top-k   exact radix select per (head, score array): one launch per 8-bit
+//          digit, each picking the previous digit from its histogram first,
+//          then a count and an ordered compaction.
 // minf_vs_index_fused runs pass 1, the fold and pass 2 in one launch instead
 // (described with its kernel below); the selection is shared.
 // No floating-point atomics are used, so two runs give identical bits.
@@ -29,6 +32,8 @@
 #include "topk.h"
 
 namespace minf {
+
+constexpr int kTkSlots = 5;   // select states per top-k array: the start and one after each digit
 
 VsWs vs_workspace(int B, int Hq, int n, int nq) {
   (void)nq;
@@ -45,8 +50,8 @@ VsWs vs_workspace(int B, int Hq, int n, int nq) {
   w.dpart = take(BH * w.nslots * kVsDiagSlots * 4);
   w.sync = take((1 + 2 * BH) * 4);
   w.tk_segs = ((int64_t)n + kTopkSeg - 1) / kTopkSeg;
-  w.tk_state = take(2 * BH * 4 * 4);
-  w.tk_hist = take(2 * BH * w.tk_segs * 256 * 4);
+  w.tk_state = take(2 * BH * kTkSlots * 4 * 4);
+  w.tk_hist = take(2 * BH * 4 * 256 * 4);
   w.tk_cnt = take(2 * BH * w.tk_segs * 2 * 4);
   w.total = off;
   return w;
@@ -759,32 +764,68 @@ __device__ __forceinline__ TkArray tk_array(const VsParams& P, int a) {
   return t;
 }
 
-// grid (2 * B * Hq): reset the select state of every array
-__global__ __launch_bounds__(64) void vs_tk_init_kernel(VsParams P) {
+// The select state of one array: slot s (s = 0..4) holds (prefix, mask,
+// remaining) after s radix digits; slot 0 is the start, slot 4 the k-th key
+// T (prefix) and the number of elements equal to T that are taken.  Digit s
+// is counted into its own 256-bin histogram (4 per array), to which every
+// segment adds its counts with integer atomics (the sums do not depend on
+// their order).  The digit of pass s is picked at the start of the next
+// launch, by every work-group of it from the same counts, so no launch does
+// the picking alone.
+__device__ __forceinline__ int32_t* tk_slot(const VsParams& P, int a, int s) {
+  return reinterpret_cast<int32_t*>(P.ws_base + P.ws.tk_state) + 4 * (kTkSlots * a + s);
+}
+__device__ __forceinline__ int32_t* tk_hist(const VsParams& P, int a, int s) {
+  return reinterpret_cast<int32_t*>(P.ws_base + P.ws.tk_hist) + 256 * (4 * a + s);
+}
+
+// The state after digit s (s = 0..3, at shift 24 - 8 s): from the state
+// before it (slot s) and the digit's histogram; every thread of the
+// work-group receives it.  Work-group 0 of the launch also stores it in
+// slot s + 1.
+__device__ void tk_pick(const VsParams& P, int a, int s, bool store, uint32_t* prefix, uint32_t* mask, int* rem) {
+  __shared__ int scan[17];
+  __shared__ uint32_t n_prefix, n_mask;
+  __shared__ int n_rem;
+  const int32_t* st = tk_slot(P, a, s);
+  const int tot = tk_hist(P, a, s)[threadIdx.x];
+  pick_digit(tot, st[2], (uint32_t)st[0], (uint32_t)st[1], 24 - 8 * s, scan, &n_prefix, &n_mask, &n_rem);
+  *prefix = n_prefix;
+  *mask = n_mask;
+  *rem = n_rem;
+  if (store && threadIdx.x == 0) {
+    int32_t* nx = tk_slot(P, a, s + 1);
+    nx[0] = (int32_t)n_prefix;
+    nx[1] = (int32_t)n_mask;
+    nx[2] = n_rem;
+  }
+}
+
+// grid (2 * B * Hq): the start state of every array, and its four digit
+// histograms cleared
+__global__ __launch_bounds__(256) void vs_tk_init_kernel(VsParams P) {
   const int a = blockIdx.x;
   const TkArray t = tk_array(P, a);
-  if (!t.vs || threadIdx.x != 0) return;
-  int32_t* st = reinterpret_cast<int32_t*>(P.ws_base + P.ws.tk_state) + 4 * a;
+  if (!t.vs) return;
+  int32_t* h = tk_hist(P, a, 0);
+  for (int i = threadIdx.x; i < 4 * 256; i += 256) h[i] = 0;
+  if (threadIdx.x != 0) return;
+  int32_t* st = tk_slot(P, a, 0);
   const bool all = t.k >= P.n;           // take every element: T = 0, all are greater or equal
   st[0] = 0;                             // prefix
   st[1] = all ? -1 : 0;                  // mask (all ones when done)
   st[2] = all ? P.n : t.k;               // remaining (elements equal to T that are taken)
 }
 
-// grid (segments, 2 * B * Hq): histogram of one radix digit (at `shift`)
-// over one segment, for the keys that match the select state so far; each
-// segment writes its own 256 bins.
-__global__ __launch_bounds__(256) void vs_tk_pass_kernel(VsParams P, int shift) {
+// grid (segments, 2 * B * Hq): digit s (at shift 24 - 8 s) of the keys of one
+// segment that match the state before it, added into the digit's histogram;
+// for s > 0 the state is first picked from digit s - 1.
+__global__ __launch_bounds__(256) void vs_tk_pass_kernel(VsParams P, int s) {
   const int seg = blockIdx.x, a = blockIdx.y;
   const TkArray t = tk_array(P, a);
   if (!t.vs || t.k <= 0 || t.k >= P.n) return;
-  const int32_t* st = reinterpret_cast<const int32_t*>(P.ws_base + P.ws.tk_state) + 4 * a;
-  int32_t* ghist = reinterpret_cast<int32_t*>(P.ws_base + P.ws.tk_hist) + ((size_t)a * P.ws.tk_segs + seg) * 256;
   __shared__ int hist[4][256];
   const int tid = threadIdx.x, wave = tid >> 6;
-  for (int i = tid; i < 4 * 256; i += 256) hist[i >> 8][i & 255] = 0;
-  const uint32_t prefix = (uint32_t)st[0], mask = (uint32_t)st[1];
-  __syncthreads();
   const int lo = seg * kTopkSeg, hi = min(lo + kTopkSeg, P.n);
   // all of the thread's loads are issued before any is used
   constexpr int E = kTopkSeg / 256;
@@ -794,6 +835,18 @@ __global__ __launch_bounds__(256) void vs_tk_pass_kernel(VsParams P, int shift) 
     const int i = lo + tid + 256 * e;
     x[e] = i < hi ? t.src[i] : 0.f;
   }
+  uint32_t prefix = 0, mask = 0;
+  int rem = 0;
+  if (s > 0) {
+    tk_pick(P, a, s - 1, seg == 0, &prefix, &mask, &rem);
+  } else {
+    const int32_t* st = tk_slot(P, a, 0);
+    prefix = (uint32_t)st[0];
+    mask = (uint32_t)st[1];
+  }
+  for (int i = tid; i < 4 * 256; i += 256) hist[i >> 8][i & 255] = 0;
+  __syncthreads();
+  const int shift = 24 - 8 * s;
   #pragma unroll
   for (int e = 0; e < E; ++e) {
     const uint32_t key = order_key(x[e]);
@@ -801,30 +854,8 @@ __global__ __launch_bounds__(256) void vs_tk_pass_kernel(VsParams P, int shift) 
     hist_add(hist[wave], m, (key >> shift) & 255u);
   }
   __syncthreads();
-  ghist[tid] = hist[0][tid] + hist[1][tid] + hist[2][tid] + hist[3][tid];
-}
-
-// grid (2 * B * Hq): sum the segments' bins and pick the digit
-__global__ __launch_bounds__(256) void vs_tk_pick_kernel(VsParams P, int shift) {
-  const int a = blockIdx.x;
-  const TkArray t = tk_array(P, a);
-  if (!t.vs || t.k <= 0 || t.k >= P.n) return;
-  int32_t* st = reinterpret_cast<int32_t*>(P.ws_base + P.ws.tk_state) + 4 * a;
-  const int32_t* ghist = reinterpret_cast<const int32_t*>(P.ws_base + P.ws.tk_hist) + (size_t)a * P.ws.tk_segs * 256;
-  __shared__ int scan[17];
-  __shared__ uint32_t n_prefix, n_mask;
-  __shared__ int n_rem;
-  const uint32_t prefix = (uint32_t)st[0], mask = (uint32_t)st[1];
-  const int rem = st[2];
-  const int segs = (int)P.ws.tk_segs;
-  int tot = 0;
-  for (int s2 = 0; s2 < segs; ++s2) tot += ghist[(size_t)s2 * 256 + threadIdx.x];
-  pick_digit(tot, rem, prefix, mask, shift, scan, &n_prefix, &n_mask, &n_rem);
-  if (threadIdx.x == 0) {
-    st[0] = (int32_t)n_prefix;
-    st[1] = (int32_t)n_mask;
-    st[2] = n_rem;
-  }
+  const int c = hist[0][tid] + hist[1][tid] + hist[2][tid] + hist[3][tid];
+  if (c) atomicAdd(tk_hist(P, a, s) + tid, c);
 }
 
 // grid (segments, 2 * B * Hq): elements above / equal to the k-th key T
@@ -832,9 +863,20 @@ __global__ __launch_bounds__(256) void vs_tk_count_kernel(VsParams P) {
   const int seg = blockIdx.x, a = blockIdx.y;
   const TkArray t = tk_array(P, a);
   if (!t.vs || t.k <= 0) return;
-  const int32_t* st = reinterpret_cast<const int32_t*>(P.ws_base + P.ws.tk_state) + 4 * a;
   int32_t* cnt = reinterpret_cast<int32_t*>(P.ws_base + P.ws.tk_cnt) + 2 * ((size_t)a * P.ws.tk_segs + seg);
-  const uint32_t T = (uint32_t)st[0];
+  // the k-th key: picked from the last digit, or (every element taken) the
+  // start state, which work-group 0 copies to the last slot
+  uint32_t T = 0, mask = 0;
+  int rem = 0;
+  if (t.k < P.n) {
+    tk_pick(P, a, 3, seg == 0, &T, &mask, &rem);
+  } else if (seg == 0 && threadIdx.x == 0) {
+    const int32_t* s0 = tk_slot(P, a, 0);
+    int32_t* s4 = tk_slot(P, a, 4);
+    s4[0] = s0[0];
+    s4[1] = s0[1];
+    s4[2] = s0[2];
+  }
   const int lo = seg * kTopkSeg, hi = min(lo + kTopkSeg, P.n);
   constexpr int E = kTopkSeg / 256;
   float x[E];
@@ -875,7 +917,7 @@ __global__ __launch_bounds__(256) void vs_tk_write_kernel(VsParams P) {
       for (int i = tid; i < t.cap; i += 256) t.out[i] = -1;
     return;
   }
-  const int32_t* st = reinterpret_cast<const int32_t*>(P.ws_base + P.ws.tk_state) + 4 * a;
+  const int32_t* st = tk_slot(P, a, 4);
   const int32_t* cnt = reinterpret_cast<const int32_t*>(P.ws_base + P.ws.tk_cnt) + 2 * (size_t)a * P.ws.tk_segs;
   const uint32_t T = (uint32_t)st[0];
   const int need_eq = st[2];
@@ -924,11 +966,8 @@ __global__ __launch_bounds__(256) void vs_tk_write_kernel(VsParams P) {
 hipError_t launch_topk(const VsParams& p, hipStream_t st) {
   const unsigned BH = (unsigned)(p.B * p.Hq);
   const dim3 tkg((unsigned)p.ws.tk_segs, 2 * BH);
-  hipLaunchKernelGGL(vs_tk_init_kernel, dim3(2 * BH), dim3(64), 0, st, p);
-  for (int shift = 24; shift >= 0; shift -= 8) {
-    hipLaunchKernelGGL(vs_tk_pass_kernel, tkg, dim3(256), 0, st, p, shift);
-    hipLaunchKernelGGL(vs_tk_pick_kernel, dim3(2 * BH), dim3(256), 0, st, p, shift);
-  }
+  hipLaunchKernelGGL(vs_tk_init_kernel, dim3(2 * BH), dim3(256), 0, st, p);
+  for (int s = 0; s < 4; ++s) hipLaunchKernelGGL(vs_tk_pass_kernel, tkg, dim3(256), 0, st, p, s);
   hipLaunchKernelGGL(vs_tk_count_kernel, tkg, dim3(256), 0, st, p);
   hipLaunchKernelGGL(vs_tk_write_kernel, tkg, dim3(256), 0, st, p);
   return hipGetLastError();
