@@ -37,8 +37,8 @@ ATTN_KERNEL = "attn_bf16_d128_kernel"
 ATTN_SOURCES = ["long_context_prefill_amd/csrc/attn_bf16.hip", "long_context_prefill_amd/csrc/common.h",
                 "long_context_prefill_amd/csrc/kernels.h", "include/minf.h"]
 ATTN_TRAFFIC = {"workload": "n128k_h32kv8_d128_bf16_mixed", "sources": "84f88fa25b3e4d54",
-                "fetch_kib": 24166308.27, "fetch_factor": 1048576 / 524303.6,
-                "write_kib": 2112675.11, "write_factor": 1048576 / 1048576.0}
+                "fetch_kib": 24463163.52, "fetch_factor": 1048576 / 524302.1,
+                "write_kib": 2112678.95, "write_factor": 1048576 / 1048576.0}
 
 
 def log(*a):
